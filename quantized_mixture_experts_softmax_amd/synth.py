@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the fused MoE expert layer.
+
+This module only draws random numbers in the shapes and dtypes of the workloads;
+it holds none of the layer's arithmetic (no routing, sorting, quantisation rule or
+GEMM).  The same bytes feed the HIP path and the CPU oracle.  bf16 activations
+come from fp32 normal draws through torch's bfloat16 cast, FP8 weight codes from a
+fixed inverse-CDF table built with torch's float8_e4m3fn cast; both are library
+conversions, not the layer's quantisers.
+
+Each tensor has its own child generator of numpy's PCG64 (SeedSequence(seed)
+spawned six ways: x, logits, w1, w1 scales, w2, w2 scales), so a tensor's values
+do not depend on the shapes of the others, and activations/logits drawn for the
+largest token count give the smaller counts as prefixes.
+
+Workloads (shapes follow the pages: w1 = fused gate/up [E, 2I, H], w2 = [E, H, I];
+MXFP4 packs two e2m1 codes per byte along K with one E8M0 byte per 32 elements;
+FP8 weights are e4m3fn bytes with fp32 scales per 128x128 block or per output
+channel):
+  tiny      T=64   H=256  I=256   E=8       top-2  MXFP4 w4a16  softmax, logits N(0,1)
+  decode    T=64   H=2880 I=2880  E=32      top-4  MXFP4 w4a16  softmax, logits N(0,1.5)
+  prefill   T=8192 H=2880 I=2880  E=128     top-4  MXFP4 w4a16  softmax, Zipf(1.1)-skewed logits
+  prefill-w4a4     same as prefill with MXFP4 activations
+  fp8-block T=4096 H=7168 I=2048  E=256(+1) top-8(+1 shared, weight 1) FP8 128x128 / act g128, sigmoid
+  fp8-channel T in {1,16,256,4096} H=4096 I=14336 E=8 top-2 FP8 per-channel / act per-token, softmax
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
+A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    topk: int
+    wfmt: int
+    afmt: int
+    score: int = SCORE_SOFTMAX
+    n_shared: int = 0
+    shared_weight: float = 1.0
+    logit_kind: str = "normal"      # "normal" or "zipf"
+    logit_std: float = 1.0
+    zipf_exponent: float = 1.1
+    seed: int = 1000
+    T_sweep: tuple = field(default_factory=tuple)
+
+    @property
+    def E_total(self) -> int:
+        return self.E + self.n_shared
+
+    @property
+    def K(self) -> int:
+        return self.topk + self.n_shared
+
+    def with_T(self, T: int) -> "Workload":
+        return Workload(**{**self.__dict__, "T": T})
+
+    def scaled(self, **kw) -> "Workload":
+        return Workload(**{**self.__dict__, **kw})
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 64, 256, 256, 8, 2, W_MXFP4, A_BF16, seed=1000),
+    "decode": Workload("decode", 64, 2880, 2880, 32, 4, W_MXFP4, A_BF16, logit_std=1.5, seed=1001),
+    "prefill": Workload("prefill", 8192, 2880, 2880, 128, 4, W_MXFP4, A_BF16, logit_kind="zipf", seed=1002),
+    "prefill-w4a4": Workload("prefill-w4a4", 8192, 2880, 2880, 128, 4, W_MXFP4, A_MXFP4_G32,
+                             logit_kind="zipf", seed=1002),
+    "fp8-block": Workload("fp8-block", 4096, 7168, 2048, 256, 8, W_FP8_BLOCK128, A_FP8_G128,
+                          score=SCORE_SIGMOID, n_shared=1, shared_weight=1.0, seed=1003),
+    "fp8-channel": Workload("fp8-channel", 4096, 4096, 14336, 8, 2, W_FP8_CHANNEL, A_FP8_TOKEN, seed=1004,
+                            T_sweep=(1, 16, 256, 4096)),
+}
+
+_FP8_STD = 112.0  # spread of the FP8 weight codes (448 / 4)
+_fp8_table = None
+
+
+def _fp8_code_table() -> np.ndarray:
+    """65536 e4m3fn codes at the quantiles of N(0, 112^2) clipped to +-448, so that
+    uniform 16-bit draws give roughly normal FP8 weight codes."""
+    global _fp8_table
+    if _fp8_table is None:
+        import torch
+        from scipy.special import ndtri
+
+        p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+        v = np.clip(ndtri(p) * _FP8_STD, -448.0, 448.0).astype(np.float32)
+        _fp8_table = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return _fp8_table
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _rngs(seed: int):
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(6)]
+
+
+def make_activations(w: Workload, T: int | None = None) -> np.ndarray:
+    """x [T, H] bf16 bits, N(0,1); a prefix of the draws for the largest T."""
+    T = w.T if T is None else T
+    rng = _rngs(w.seed)[0]
+    return f32_to_bf16_bits(rng.standard_normal((T, w.H), dtype=np.float32))
+
+
+def make_logits(w: Workload, T: int | None = None) -> np.ndarray:
+    """Router logits [T, E] fp32.  "zipf": expert popularity p_e proportional to
+    r_e^-s with ranks r a seeded permutation of 1..E, logits = ln p_e + Gumbel(0,1),
+    so the top-1 choice is distributed exactly as p (Gumbel-max)."""
+    T = w.T if T is None else T
+    rng = _rngs(w.seed)[1]
+    if w.logit_kind == "normal":
+        return rng.normal(0.0, w.logit_std, (T, w.E)).astype(np.float32)
+    ranks = rng.permutation(w.E).astype(np.float64) + 1.0
+    logp = -w.zipf_exponent * np.log(ranks)
+    logp -= np.log(np.exp(logp).sum())
+    g = rng.gumbel(0.0, 1.0, (T, w.E))
+    return (logp[None, :] + g).astype(np.float32)
+
+
+def _weight(w: Workload, N: int, K: int, rng_codes, rng_scales):
+    """One [E_total, N, K] weight tensor in the workload's format."""
+    E = w.E_total
+    if w.wfmt == W_MXFP4:
+        codes = rng_codes.integers(0, 256, (E, N, K // 2), dtype=np.uint8)   # two uniform nibbles per byte
+        scales = rng_scales.integers(118, 127, (E, N, K // 32), dtype=np.uint8)  # E8M0 exponent in [118, 126]
+        return codes, scales
+    table = _fp8_code_table()
+    codes = np.empty((E, N, K), np.uint8)
+    for e in range(E):
+        idx = rng_codes.integers(0, 65536, (N, K), dtype=np.uint16)
+        codes[e] = table[idx]
+    base = 1.0 / (_FP8_STD * math.sqrt(K))
+    if w.wfmt == W_FP8_BLOCK128:
+        scales = (rng_scales.uniform(0.75, 1.25, (E, (N + 127) // 128, (K + 127) // 128)) * base).astype(np.float32)
+    else:
+        scales = (rng_scales.uniform(0.75, 1.25, (E, N)) * base).astype(np.float32)
+    return codes, scales
+
+
+def make_weights(w: Workload):
+    """(w1, w1_scale, w2, w2_scale) host arrays; w1 rows [0, I) gate, [I, 2I) up."""
+    r = _rngs(w.seed)
+    w1, w1s = _weight(w, 2 * w.I, w.H, r[2], r[3])
+    w2, w2s = _weight(w, w.H, w.I, r[4], r[5])
+    return w1, w1s, w2, w2s
+
+
+def make_all(w: Workload, T: int | None = None) -> dict:
+    T = w.T if T is None else T
+    w1, w1s, w2, w2s = make_weights(w)
+    return dict(x=make_activations(w, T), logits=make_logits(w, T), w1=w1, w1_scale=w1s, w2=w2, w2_scale=w2s)
