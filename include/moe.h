@@ -1,0 +1,208 @@
+/*
+ * libmoe -- quantized fused Mixture-of-Experts expert layer for AMD MI355X (gfx950).
+ *
+ * C ABI.  Pages cited by title and section:
+ *   [rocm_aiter_moe]  vLLM API page "vllm.model_executor.layers.fused_moe.experts.rocm_aiter_moe"
+ *   [mxfp4.py]        vLLM source page "vllm/model_executor/layers/quantization/mxfp4.py"
+ *   [quark_moe]       vLLM API page "vllm.model_executor.layers.quantization.quark.quark_moe"
+ *
+ * General rules for every entry point below:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; tensors are dense
+ *     row-major.  The library keeps no pointer after a call returns.
+ *   - Calls only enqueue work on `stream` (NULL = the null stream).  They never
+ *     allocate device memory, never synchronise the host and never read device
+ *     data on the host, so a call may be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     non-MOE_OK status nothing was enqueued and moe_last_error() returns a
+ *     message for the calling thread.  Invalid DEVICE data (an expert id out of
+ *     range in topk_ids, NaN logits) is not an error: such slots are dropped as
+ *     documented per call.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on
+ *     every call (no floating-point atomics anywhere).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* bad shape, pointer, alignment or enum */
+  MOE_EUNSUPPORTED = 2,  /* valid request this library does not implement */
+  MOE_EWORKSPACE = 3,    /* workspace missing or smaller than moe_experts_workspace_bytes() */
+  MOE_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+/* Router score function.  The pages name the softmax top-k router only through its
+ * products ([rocm_aiter_moe] inject_shared_expert_weights, rocm_aiter_fused_experts);
+ * sigmoid scoring is the DeepSeek-style variant. */
+typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Weight formats ([rocm_aiter_moe] derive_aiter_quant_method):
+ *   MOE_W_MXFP4        BLOCK_1X32: w1 uint8 [E, 2I, H/2] (two e2m1 codes per byte, the low
+ *                      nibble holds the even K index), w1_scale uint8 E8M0 [E, 2I, H/32];
+ *                      w2 [E, H, I/2], w2_scale [E, H, I/32]  ([mxfp4.py] Mxfp4MoEMethod.create_weights)
+ *   MOE_W_FP8_BLOCK128 BLOCK_128x128: w1 e4m3fn [E, 2I, H], w1_scale fp32 [E, ceil(2I/128), ceil(H/128)];
+ *                      w2 [E, H, I], w2_scale fp32 [E, ceil(H/128), ceil(I/128)]  ([rocm_aiter_moe] AiterFp8BlockExperts)
+ *   MOE_W_FP8_CHANNEL  PER_TOKEN (per output channel): codes as above, w1_scale fp32 [E, 2I],
+ *                      w2_scale fp32 [E, H]  ([rocm_aiter_moe] AiterFp8ChannelExperts)
+ * In w1 rows [0, I) are the gate projection and rows [I, 2I) the up projection. */
+typedef enum moe_wfmt { MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANNEL = 2 } moe_wfmt;
+
+/* Activation (GEMM input) formats, quantised dynamically ([rocm_aiter_moe]
+ * AiterMxfp4Experts, AiterFp8BlockExperts, AiterFp8ChannelExperts):
+ *   MOE_A_BF16       no quantisation (w4a16)
+ *   MOE_A_MXFP4_G32  codes uint8 [rows, cols/2] (two e2m1 per byte, low nibble = even column),
+ *                    scales uint8 E8M0 [rows, cols/32]
+ *   MOE_A_FP8_G128   codes e4m3fn [rows, cols], scales fp32 [rows, ceil(cols/128)]
+ *   MOE_A_FP8_TOKEN  codes e4m3fn [rows, cols], scales fp32 [rows] */
+typedef enum moe_afmt { MOE_A_BF16 = 0, MOE_A_MXFP4_G32 = 1, MOE_A_FP8_G128 = 2, MOE_A_FP8_TOKEN = 3 } moe_afmt;
+
+/* Gated activation.  Only SiLU-and-mul: h = silu(gate) * up, silu(z) = z / (1 + e^-z)
+ * ([rocm_aiter_moe] AiterExperts: SILU activation, act-and-mul only). */
+typedef enum moe_act { MOE_ACT_SILU = 0 } moe_act;
+
+/* ------------------------------------------------------------------------------------
+ * moe_route_topk -- softmax / sigmoid top-k router with optional shared-expert slots.
+ *
+ * For every token t: the `topk` largest logits of router_logits[t, 0:E] in descending
+ * order (equal logits: lower expert id first).  Weights:
+ *   softmax: exp(l_j - l_max) / sum, the sum over the chosen k when `renormalize`
+ *            (equal to the renormalised full softmax), else over all E logits;
+ *   sigmoid: 1 / (1 + exp(-l_j)), divided by their sum over the chosen k when `renormalize`.
+ * Then n_shared shared-expert slots follow: slot topk + s holds expert id E + s with
+ * weight shared_weight, the combined routed+shared layout of [rocm_aiter_moe]
+ * inject_shared_expert_weights.
+ *   router_logits  [T, E] fp32 (input of [mxfp4.py] Mxfp4MoEMethod.apply_monolithic)
+ *   topk_ids       [T, topk + n_shared] int32   (written)
+ *   topk_weights   [T, topk + n_shared] fp32    (written; dtypes as cast in
+ *                  [rocm_aiter_moe] rocm_aiter_fused_experts)
+ * Limits: 1 <= E <= 1024, 1 <= topk <= min(E, 32), 0 <= n_shared <= 32, T >= 0.
+ * T == 0 enqueues nothing.  Logits must be finite (NaN rows give unspecified ids).
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_route_topk(const float* router_logits, int T, int E, int topk, moe_score score,
+                          int renormalize, int n_shared, float shared_weight,
+                          int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_align_sort -- stable token->expert sort padded to the GEMM row tile.
+ *
+ * The flattened slots s = t*K + j (K = slots per token, routed + shared) are grouped by
+ * expert id in ascending slot order; each expert's run is padded up to a multiple of
+ * block_m rows.  The pages hand this step to the fused kernel as its "moe sorting"
+ * dispatch policy and per-expert token counts ([rocm_aiter_moe] rocm_aiter_fused_experts,
+ * AiterExperts.apply: expert_num_tokens).
+ *   topk_ids        [T, K] int32 (input)
+ *   expert_counts   [E_total] int32: slots routed to each expert
+ *   expert_offsets  [E_total + 1] int32: first padded row of each expert; the last entry
+ *                   is the total number of padded rows
+ *   sorted_slots    [moe_sort_capacity(T,K,E_total,block_m)] int32: slot id per padded row,
+ *                   T*K for pad rows and for every row past the total
+ *   block_expert    [moe_sort_capacity(...) / block_m] int32: owning expert of each
+ *                   block of block_m rows, -1 past the total
+ *   num_padded      [1] int32: total padded rows (= expert_offsets[E_total])
+ * Limits: E_total <= 1024, block_m in {16, 32, 64, 128}, T*K < 2^31 - E_total*block_m.
+ * Ids outside [0, E_total) are not placed (their slots are skipped by the layer).
+ * ---------------------------------------------------------------------------------- */
+size_t moe_sort_capacity(int T, int K, int E_total, int block_m); /* = T*K + E_total*(block_m-1) */
+moe_status moe_align_sort(const int32_t* topk_ids, int T, int K, int E_total, int block_m,
+                          int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                          int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_quant_act -- dynamic activation quantisation of a bf16 matrix [rows, cols].
+ *
+ * FP8 (e4m3fn) formats: per group (128 columns, or the whole row for MOE_A_FP8_TOKEN;
+ * the last 128-group of a row may be shorter), s = amax / 448 in IEEE fp32 (s = 1 for an
+ * all-zero group) and code = nearest e4m3fn value of x / s (IEEE fp32 division), ties to
+ * even, saturating at +-448 ([rocm_aiter_moe] AiterFp8BlockExperts: 128-grouped dynamic
+ * activation scale; AiterFp8ChannelExperts: per-token dynamic scale).
+ * MXFP4: per 32 columns, shared exponent es = floor(log2 amax) - 2 clamped to [-127, 127]
+ * (es = -127 for an all-zero group), scale byte es + 127, code = nearest e2m1 of
+ * x * 2^-es, ties to even, saturating at +-6 ([rocm_aiter_moe] AiterMxfp4Experts,
+ * MXFP4 dynamic activations; two codes per byte as [quark_moe]
+ * QuarkOCP_MX_MoEMethod.get_packed_dim).  The code's sign bit is the sign of x.
+ *   x       [rows, cols] bf16;  codes / scales: layouts of moe_afmt above.
+ * Limits: cols % 32 == 0, cols <= 65536, rows >= 0.  fmt == MOE_A_BF16 is MOE_EINVAL.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
+                         uint8_t* codes, void* scales, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_experts_forward -- the expert computation of the fused MoE layer.
+ *
+ * For every slot (t, j) routed to expert e = topk_ids[t, j] (shared experts are ordinary
+ * experts with ids >= the routed count, carried as extra slots):
+ *   stage 1  [g | u] = a1[t] . w1[e]^T   (g: rows [0, I) of w1, u: rows [I, 2I))
+ *            h = bf16( silu(g) * u )      fused into the GEMM epilogue
+ *            for quantised activation formats h is re-quantised (a2) in the same format
+ *   stage 2  y = a2 . w2[e]^T, scaled by topk_weights[t, j]
+ *   out[t] = bf16( sum over j = 0..K-1, in ascending j, of the weighted y )
+ * (the weighted reduction is part of the expert computation: [rocm_aiter_moe]
+ * AiterExperts.finalize_weight_and_reduce_impl is a no-op and the weights apply to the
+ * second GEMM's output by default, per AiterFp8ChannelExperts.apply.)
+ * a1 is hidden_states itself (MOE_A_BF16) or its quantisation; pass a1_codes/a1_scales
+ * from moe_quant_act, or NULL to quantise inside this call.
+ * Rows come from moe_align_sort run with the same T, K, E_total and block_m.
+ * The workspace holds the intermediate h, the a1/a2 codes and an fp32 per-slot buffer
+ * [T*K, H]; its layout is reported by moe_workspace_layout().
+ * Limits: H % 32 == 0, I % 32 == 0, H, I <= 65536, 1 <= K <= 64, E_total <= 1024,
+ * block_m in {16, 32, 64, 128}; (wfmt, afmt) one of
+ *   (MXFP4, BF16) (MXFP4, MXFP4_G32) (FP8_BLOCK128, FP8_G128) (FP8_CHANNEL, FP8_TOKEN)
+ * (others: MOE_EUNSUPPORTED).  Pointers to 16-byte aligned memory.
+ * ---------------------------------------------------------------------------------- */
+typedef struct moe_forward_args {
+  int T, H, I, E_total, K, block_m;
+  moe_wfmt wfmt;
+  moe_afmt afmt;
+  moe_act act;
+  const uint16_t* hidden_states;                 /* [T, H] bf16 */
+  const uint8_t* a1_codes; const void* a1_scales; /* optional pre-quantised hidden_states */
+  const uint8_t* w1; const void* w1_scale;       /* see moe_wfmt */
+  const uint8_t* w2; const void* w2_scale;
+  const int32_t* topk_ids;                       /* [T, K] */
+  const float* topk_weights;                     /* [T, K] */
+  const int32_t* sorted_slots;                   /* from moe_align_sort */
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  uint16_t* out;                                 /* [T, H] bf16, written */
+  void* workspace;
+  size_t workspace_bytes;
+} moe_forward_args;
+
+/* Byte offsets into the workspace (each 256-byte aligned); 0 size = not used. */
+typedef struct moe_workspace_layout_t {
+  size_t h_off, h_bytes;           /* bf16 [cap, I]: stage-1 output in sorted-row order */
+  size_t a1_codes_off, a1_codes_bytes, a1_scales_off, a1_scales_bytes; /* quantised hidden_states */
+  size_t a2_codes_off, a2_codes_bytes, a2_scales_off, a2_scales_bytes; /* quantised h, sorted rows */
+  size_t ybuf_off, ybuf_bytes;     /* fp32 [T*K, H]: weighted stage-2 rows by slot id */
+  size_t total;
+} moe_workspace_layout_t;
+
+size_t moe_experts_workspace_bytes(const moe_forward_args* a);
+moe_status moe_workspace_layout(const moe_forward_args* a, moe_workspace_layout_t* layout);
+moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream);
+
+/* Whether a (wfmt, afmt, act, H, I) combination is implemented (MOE_OK) or not
+ * (MOE_EUNSUPPORTED / MOE_EINVAL, with the reason in moe_last_error()); the analogue of
+ * [rocm_aiter_moe] AiterExperts.is_supported_config. */
+moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I);
+
+/* A row tile for moe_align_sort / moe_experts_forward suited to T*K slots over E_total
+ * experts (host-side heuristic; any value in {16, 32, 64, 128} is valid). */
+int moe_pick_block_m(int T, int K, int E_total);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

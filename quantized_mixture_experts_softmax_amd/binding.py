@@ -1,0 +1,297 @@
+"""Python binding of libmoe (include/moe.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module allocates outputs and the
+workspace with torch on the tensors' device and passes raw device pointers and the
+current HIP stream.  If libmoe.so is missing or cannot be loaded, every entry point
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
+SCORE = {"softmax": 0, "sigmoid": 1}
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
+A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
+ACT_SILU = 0
+
+EXPORTED = [
+    "moe_route_topk", "moe_sort_capacity", "moe_align_sort", "moe_quant_act",
+    "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
+    "moe_supports", "moe_pick_block_m", "moe_last_error",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmoe status {status}: {msg}")
+        self.status = status
+
+
+class ForwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int), ("E_total", ctypes.c_int),
+        ("K", ctypes.c_int), ("block_m", ctypes.c_int),
+        ("wfmt", ctypes.c_int), ("afmt", ctypes.c_int), ("act", ctypes.c_int),
+        ("hidden_states", ctypes.c_void_p),
+        ("a1_codes", ctypes.c_void_p), ("a1_scales", ctypes.c_void_p),
+        ("w1", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+        ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+        ("sorted_slots", ctypes.c_void_p), ("block_expert", ctypes.c_void_p), ("num_padded", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "h_off", "h_bytes", "a1_codes_off", "a1_codes_bytes", "a1_scales_off", "a1_scales_bytes",
+        "a2_codes_off", "a2_codes_bytes", "a2_scales_off", "a2_scales_bytes", "ybuf_off", "ybuf_bytes", "total")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it is not built.  There is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmoe.so not found at {LIB_PATH}; run "
+                               "`python -m quantized_mixture_experts_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int
+        L.moe_route_topk.restype = S
+        L.moe_route_topk.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, P, P, P]
+        L.moe_sort_capacity.restype = ctypes.c_size_t
+        L.moe_sort_capacity.argtypes = [I, I, I, I]
+        L.moe_align_sort.restype = S
+        L.moe_align_sort.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
+        L.moe_quant_act.restype = S
+        L.moe_quant_act.argtypes = [P, I, I, I, P, P, P]
+        L.moe_experts_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_experts_workspace_bytes.argtypes = [ctypes.POINTER(ForwardArgs)]
+        L.moe_workspace_layout.restype = S
+        L.moe_workspace_layout.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.POINTER(WorkspaceLayout)]
+        L.moe_experts_forward.restype = S
+        L.moe_experts_forward.argtypes = [ctypes.POINTER(ForwardArgs), P]
+        L.moe_supports.restype = S
+        L.moe_supports.argtypes = [I, I, I, I, I]
+        L.moe_pick_block_m.restype = I
+        L.moe_pick_block_m.argtypes = [I, I, I]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(st: int) -> None:
+    if st != MOE_OK:
+        raise MoeError(st, lib().moe_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libmoe tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor) -> torch.device:
+    if t.device.type != "cuda":
+        raise ValueError("libmoe tensors must live on the GPU")
+    return t.device
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_supports(wfmt: int, afmt: int, H: int, I: int, act: int = ACT_SILU) -> bool:
+    return lib().moe_supports(wfmt, afmt, act, H, I) == MOE_OK
+
+
+def moe_pick_block_m(T: int, K: int, E_total: int) -> int:
+    return lib().moe_pick_block_m(T, K, E_total)
+
+
+def moe_sort_capacity(T: int, K: int, E_total: int, block_m: int) -> int:
+    return lib().moe_sort_capacity(T, K, E_total, block_m)
+
+
+def moe_route_topk(router_logits: torch.Tensor, topk: int, score: str = "softmax", renormalize: bool = True,
+                   n_shared: int = 0, shared_weight: float = 1.0, topk_ids=None, topk_weights=None, stream=None):
+    dev = _dev(router_logits)
+    assert router_logits.dtype == torch.float32 and router_logits.dim() == 2
+    T, E = router_logits.shape
+    KP = topk + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty((T, KP), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, KP), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_topk(_ptr(router_logits), T, E, topk, SCORE[score], int(renormalize), n_shared,
+                                shared_weight, _ptr(topk_ids), _ptr(topk_weights), _stream(stream, dev)))
+    return topk_ids, topk_weights
+
+
+def moe_align_sort(topk_ids: torch.Tensor, E_total: int, block_m: int, out: dict | None = None, stream=None) -> dict:
+    dev = _dev(topk_ids)
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2
+    T, K = topk_ids.shape
+    cap = moe_sort_capacity(T, K, E_total, block_m)
+    if out is None:
+        out = dict(
+            expert_counts=torch.empty(E_total, dtype=torch.int32, device=dev),
+            expert_offsets=torch.empty(E_total + 1, dtype=torch.int32, device=dev),
+            sorted_slots=torch.empty(cap, dtype=torch.int32, device=dev),
+            block_expert=torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+            num_padded=torch.empty(1, dtype=torch.int32, device=dev),
+        )
+    _check(lib().moe_align_sort(_ptr(topk_ids), T, K, E_total, block_m, _ptr(out["expert_counts"]),
+                                _ptr(out["expert_offsets"]), _ptr(out["sorted_slots"]), _ptr(out["block_expert"]),
+                                _ptr(out["num_padded"]), _stream(stream, dev)))
+    return out
+
+
+def quant_shapes(fmt: int, rows: int, cols: int):
+    if fmt == A_MXFP4_G32:
+        return (rows, cols // 2), (rows, cols // 32), torch.uint8
+    if fmt == A_FP8_G128:
+        return (rows, cols), (rows, (cols + 127) // 128), torch.float32
+    if fmt == A_FP8_TOKEN:
+        return (rows, cols), (rows,), torch.float32
+    raise ValueError("bf16 activations have no quantiser")
+
+
+def moe_quant_act(x: torch.Tensor, fmt: int, codes=None, scales=None, stream=None):
+    dev = _dev(x)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    rows, cols = x.shape
+    cs, ss, sdt = quant_shapes(fmt, rows, cols)
+    if codes is None:
+        codes = torch.empty(cs, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(ss, dtype=sdt, device=dev)
+    _check(lib().moe_quant_act(_ptr(x), rows, cols, fmt, _ptr(codes), _ptr(scales), _stream(stream, dev)))
+    return codes, scales
+
+
+def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
+                 afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
+                 a1_scales=None) -> ForwardArgs:
+    T, H = hidden_states.shape
+    K = topk_ids.shape[1]
+    a = ForwardArgs()
+    a.T, a.H, a.I, a.E_total, a.K, a.block_m = T, H, I, E_total, K, block_m
+    a.wfmt, a.afmt, a.act = wfmt, afmt, ACT_SILU
+    a.hidden_states = _ptr(hidden_states)
+    a.a1_codes, a.a1_scales = _ptr(a1_codes), _ptr(a1_scales)
+    a.w1, a.w1_scale, a.w2, a.w2_scale = _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale)
+    a.topk_ids, a.topk_weights = _ptr(topk_ids), _ptr(topk_weights)
+    a.sorted_slots, a.block_expert, a.num_padded = (_ptr(sort["sorted_slots"]), _ptr(sort["block_expert"]),
+                                                    _ptr(sort["num_padded"]))
+    a.out = _ptr(out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return a
+
+
+def moe_experts_workspace_bytes(args: ForwardArgs) -> int:
+    n = lib().moe_experts_workspace_bytes(ctypes.byref(args))
+    if n == 0:
+        _check(lib().moe_workspace_layout(ctypes.byref(args), ctypes.byref(WorkspaceLayout())))
+    return n
+
+
+def moe_workspace_layout(args: ForwardArgs) -> dict:
+    L = WorkspaceLayout()
+    _check(lib().moe_workspace_layout(ctypes.byref(args), ctypes.byref(L)))
+    return {n: getattr(L, n) for n, _ in WorkspaceLayout._fields_}
+
+
+def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
+                        afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
+                        a1_scales=None, stream=None):
+    """Returns (out, workspace).  The workspace may be passed back in on later calls."""
+    dev = _dev(hidden_states)
+    assert hidden_states.dtype == torch.bfloat16
+    T, H = hidden_states.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    args = forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort, wfmt, afmt,
+                        block_m, E_total, I, out, workspace, a1_codes, a1_scales)
+    need = moe_experts_workspace_bytes(args)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(lib().moe_experts_forward(ctypes.byref(args), _stream(stream, dev)))
+    return out, workspace
+
+
+class MoELayer:
+    """Device-resident weights of one quantised MoE expert layer and the full hot
+    path (route -> align-sort -> optional a1 quantisation -> experts forward), each
+    step one libmoe call.  Buffers are allocated on first use and reused."""
+
+    def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
+                 score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None):
+        self.w1, self.w1_scale, self.w2, self.w2_scale = w1, w1_scale, w2, w2_scale
+        self.H, self.I, self.E, self.topk = H, I, E, topk
+        self.wfmt, self.afmt, self.score = wfmt, afmt, score
+        self.n_shared, self.shared_weight = n_shared, shared_weight
+        self.E_total = E + n_shared
+        self.K = topk + n_shared
+        self.block_m = block_m
+        self._bufs: dict = {}
+
+    def _buffers(self, T: int, dev):
+        key = (T, str(dev))
+        if key not in self._bufs:
+            bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total)
+            cap = moe_sort_capacity(T, self.K, self.E_total, bm)
+            b = dict(
+                bm=bm,
+                ids=torch.empty((T, self.K), dtype=torch.int32, device=dev),
+                w=torch.empty((T, self.K), dtype=torch.float32, device=dev),
+                sort=dict(
+                    expert_counts=torch.empty(self.E_total, dtype=torch.int32, device=dev),
+                    expert_offsets=torch.empty(self.E_total + 1, dtype=torch.int32, device=dev),
+                    sorted_slots=torch.empty(cap, dtype=torch.int32, device=dev),
+                    block_expert=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
+                    num_padded=torch.empty(1, dtype=torch.int32, device=dev)),
+                out=torch.empty((T, self.H), dtype=torch.bfloat16, device=dev),
+                workspace=None, a1=None,
+            )
+            if self.afmt != A_BF16:
+                cs, ss, sdt = quant_shapes(self.afmt, T, self.H)
+                b["a1"] = (torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=sdt, device=dev))
+            self._bufs = {key: b}
+        return self._bufs[key]
+
+    def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        b = self._buffers(T, x.device)
+        moe_route_topk(router_logits, self.topk, self.score, True, self.n_shared, self.shared_weight,
+                       b["ids"], b["w"], stream)
+        moe_align_sort(b["ids"], self.E_total, b["bm"], b["sort"], stream)
+        a1c = a1s = None
+        if self.afmt != A_BF16:
+            a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
+        out, b["workspace"] = moe_experts_forward(
+            x, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"], self.wfmt, self.afmt,
+            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream)
+        return out

@@ -1,0 +1,272 @@
+// C-ABI entry points of libmoe: host-side validation, workspace layout and the
+// launch sequence.  Nothing here allocates, synchronises or reads device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// bytes of codes / scales of a [rows, cols] matrix in activation format f
+size_t code_bytes(int f, size_t rows, size_t cols) {
+  if (f == MOE_A_MXFP4_G32) return rows * cols / 2;
+  if (f == MOE_A_FP8_G128 || f == MOE_A_FP8_TOKEN) return rows * cols;
+  return 0;
+}
+size_t scale_bytes(int f, size_t rows, size_t cols) {
+  if (f == MOE_A_MXFP4_G32) return rows * (cols / 32);
+  if (f == MOE_A_FP8_G128) return rows * ((cols + 127) / 128) * 4;
+  if (f == MOE_A_FP8_TOKEN) return rows * 4;
+  return 0;
+}
+
+bool pair_supported(int wf, int af) {
+  return (wf == MOE_W_MXFP4 && (af == MOE_A_BF16 || af == MOE_A_MXFP4_G32)) ||
+         (wf == MOE_W_FP8_BLOCK128 && af == MOE_A_FP8_G128) || (wf == MOE_W_FP8_CHANNEL && af == MOE_A_FP8_TOKEN);
+}
+
+moe_status check_shapes(const moe_forward_args* a) {
+  if (!a) return fail(MOE_EINVAL, "moe_experts_forward: args is NULL");
+  if (a->T < 0) return fail(MOE_EINVAL, "T must be >= 0 (got %d)", a->T);
+  if (a->H <= 0 || a->H % 32 || a->H > 65536) return fail(MOE_EINVAL, "H must be a positive multiple of 32 <= 65536 (got %d)", a->H);
+  if (a->I <= 0 || a->I % 32 || a->I > 65536) return fail(MOE_EINVAL, "I must be a positive multiple of 32 <= 65536 (got %d)", a->I);
+  if (a->E_total < 1 || a->E_total > 1024) return fail(MOE_EINVAL, "E_total must be in [1, 1024] (got %d)", a->E_total);
+  if (a->K < 1 || a->K > 64) return fail(MOE_EINVAL, "K must be in [1, 64] (got %d)", a->K);
+  if (!valid_bm(a->block_m)) return fail(MOE_EINVAL, "block_m must be 16, 32, 64 or 128 (got %d)", a->block_m);
+  if ((long long)a->T * a->K + (long long)a->E_total * a->block_m >= 0x7FFFFFFFLL)
+    return fail(MOE_EINVAL, "T*K too large");
+  if (a->act != MOE_ACT_SILU) return fail(MOE_EUNSUPPORTED, "only the SiLU-and-mul activation is implemented");
+  if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
+  if (a->afmt < MOE_A_BF16 || a->afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)a->afmt);
+  if (!pair_supported(a->wfmt, a->afmt))
+    return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)a->wfmt,
+                (int)a->afmt);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I) {
+  if (act != MOE_ACT_SILU) return fail(MOE_EUNSUPPORTED, "only the SiLU-and-mul activation is implemented");
+  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
+  if (afmt < MOE_A_BF16 || afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)afmt);
+  if (!pair_supported(wfmt, afmt))
+    return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)wfmt, (int)afmt);
+  if (H <= 0 || H % 32 || I <= 0 || I % 32 || H > 65536 || I > 65536)
+    return fail(MOE_EINVAL, "H and I must be positive multiples of 32 <= 65536 (got %d, %d)", H, I);
+  return ok();
+}
+
+int moe_pick_block_m(int T, int K, int E_total) {
+  if (E_total <= 0) return 16;
+  const double rows = (double)T * K / E_total;
+  if (rows <= 16) return 16;
+  if (rows <= 48) return 32;
+  if (rows <= 96) return 64;
+  return 128;
+}
+
+moe_status moe_route_topk(const float* router_logits, int T, int E, int topk, moe_score score, int renormalize,
+                          int n_shared, float shared_weight, int32_t* topk_ids, float* topk_weights,
+                          hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_route_topk: T must be >= 0 (got %d)", T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "moe_route_topk: E must be in [1, 1024] (got %d)", E);
+  if (topk < 1 || topk > E || topk > 32) return fail(MOE_EINVAL, "moe_route_topk: topk must be in [1, min(E, 32)] (got %d)", topk);
+  if (n_shared < 0 || n_shared > 32) return fail(MOE_EINVAL, "moe_route_topk: n_shared must be in [0, 32] (got %d)", n_shared);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return fail(MOE_EINVAL, "moe_route_topk: unknown score %d", (int)score);
+  if (T > 0 && (!router_logits || !topk_ids || !topk_weights)) return fail(MOE_EINVAL, "moe_route_topk: NULL pointer");
+  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "moe_route_topk: pointers must be 4-byte aligned");
+  return hip_status(moe::launch_route_topk(router_logits, T, E, topk, (int)score, renormalize ? 1 : 0, n_shared,
+                                           shared_weight, topk_ids, topk_weights, stream),
+                    "moe_route_topk launch");
+}
+
+size_t moe_sort_capacity(int T, int K, int E_total, int block_m) {
+  if (T < 0 || K < 0 || E_total < 0 || block_m < 1) return 0;
+  return (size_t)T * K + (size_t)E_total * (block_m - 1);
+}
+
+moe_status moe_align_sort(const int32_t* topk_ids, int T, int K, int E_total, int block_m, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_slots, int32_t* block_expert, int32_t* num_padded,
+                          hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_align_sort: T must be >= 0 (got %d)", T);
+  if (K < 1 || K > 64) return fail(MOE_EINVAL, "moe_align_sort: K must be in [1, 64] (got %d)", K);
+  if (E_total < 1 || E_total > 1024) return fail(MOE_EINVAL, "moe_align_sort: E_total must be in [1, 1024] (got %d)", E_total);
+  if (!valid_bm(block_m)) return fail(MOE_EINVAL, "moe_align_sort: block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+  if ((long long)T * K + (long long)E_total * block_m >= 0x7FFFFFFFLL) return fail(MOE_EINVAL, "moe_align_sort: T*K too large");
+  if (!expert_counts || !expert_offsets || !sorted_slots || !block_expert || !num_padded || (T > 0 && !topk_ids))
+    return fail(MOE_EINVAL, "moe_align_sort: NULL pointer");
+  return hip_status(moe::launch_align_sort(topk_ids, T, K, E_total, block_m, expert_counts, expert_offsets,
+                                           sorted_slots, block_expert, num_padded, stream),
+                    "moe_align_sort launch");
+}
+
+moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt, uint8_t* codes, void* scales,
+                         hipStream_t stream) {
+  if (fmt != MOE_A_MXFP4_G32 && fmt != MOE_A_FP8_G128 && fmt != MOE_A_FP8_TOKEN)
+    return fail(MOE_EINVAL, "moe_quant_act: format %d has no quantiser", (int)fmt);
+  if (rows < 0) return fail(MOE_EINVAL, "moe_quant_act: rows must be >= 0 (got %d)", rows);
+  if (cols <= 0 || cols % 32 || cols > 65536) return fail(MOE_EINVAL, "moe_quant_act: cols must be a positive multiple of 32 <= 65536 (got %d)", cols);
+  if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_EINVAL, "moe_quant_act: NULL pointer");
+  if (!aligned(x, 4) || !aligned(codes, 2) || !aligned(scales, 4)) return fail(MOE_EINVAL, "moe_quant_act: misaligned pointer");
+  return hip_status(moe::launch_quant_act(x, rows, cols, (int)fmt, nullptr, codes, scales, stream), "moe_quant_act launch");
+}
+
+moe_status moe_workspace_layout(const moe_forward_args* a, moe_workspace_layout_t* L) {
+  moe_status st = check_shapes(a);
+  if (st != MOE_OK) return st;
+  if (!L) return fail(MOE_EINVAL, "moe_workspace_layout: layout is NULL");
+  memset(L, 0, sizeof *L);
+  const size_t cap = moe_sort_capacity(a->T, a->K, a->E_total, a->block_m);
+  size_t off = 0;
+  auto take = [&](size_t bytes, size_t& o, size_t& b) {
+    b = bytes;
+    o = bytes ? off : 0;
+    off = round_up(off + bytes, 256);
+  };
+  take(cap * (size_t)a->I * 2, L->h_off, L->h_bytes);
+  if (a->afmt != MOE_A_BF16 && a->a1_codes == nullptr) {
+    take(code_bytes(a->afmt, a->T, a->H), L->a1_codes_off, L->a1_codes_bytes);
+    take(scale_bytes(a->afmt, a->T, a->H), L->a1_scales_off, L->a1_scales_bytes);
+  }
+  if (a->afmt != MOE_A_BF16) {
+    take(code_bytes(a->afmt, cap, a->I), L->a2_codes_off, L->a2_codes_bytes);
+    take(scale_bytes(a->afmt, cap, a->I), L->a2_scales_off, L->a2_scales_bytes);
+  }
+  take((size_t)a->T * a->K * a->H * 4, L->ybuf_off, L->ybuf_bytes);
+  L->total = off;
+  return ok();
+}
+
+size_t moe_experts_workspace_bytes(const moe_forward_args* a) {
+  moe_workspace_layout_t L;
+  if (moe_workspace_layout(a, &L) != MOE_OK) return 0;
+  return L.total;
+}
+
+moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
+  moe_workspace_layout_t L;
+  moe_status st = moe_workspace_layout(a, &L);
+  if (st != MOE_OK) return st;
+  if (a->T == 0) return ok();
+  if (!a->hidden_states || !a->w1 || !a->w1_scale || !a->w2 || !a->w2_scale || !a->topk_ids || !a->topk_weights ||
+      !a->sorted_slots || !a->block_expert || !a->num_padded || !a->out)
+    return fail(MOE_EINVAL, "moe_experts_forward: NULL pointer");
+  if (!aligned(a->hidden_states, 16) || !aligned(a->w1, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
+      !aligned(a->topk_weights, 4) || !aligned(a->w1_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) ||
+      !aligned(a->w2_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) || (a->a1_codes && !aligned(a->a1_codes, 16)) ||
+      (a->a1_scales && !aligned(a->a1_scales, 4)))
+    return fail(MOE_EINVAL, "moe_experts_forward: misaligned pointer (16 B for tensors, 4 B for fp32 arrays)");
+  if (a->afmt != MOE_A_BF16 && (a->a1_codes == nullptr) != (a->a1_scales == nullptr))
+    return fail(MOE_EINVAL, "moe_experts_forward: a1_codes and a1_scales go together");
+  if (!a->workspace || a->workspace_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "moe_experts_forward: workspace of %zu bytes needed, %zu given", L.total,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  if (!aligned(a->workspace, 256)) return fail(MOE_EINVAL, "moe_experts_forward: workspace must be 256-byte aligned");
+
+  uint8_t* ws = (uint8_t*)a->workspace;
+  const size_t cap = moe_sort_capacity(a->T, a->K, a->E_total, a->block_m);
+  const int afmt = (int)a->afmt;
+  uint16_t* h = (uint16_t*)(ws + L.h_off);
+  const void* a1 = a->hidden_states;
+  const void* a1s = nullptr;
+  hipError_t e = hipSuccess;
+  if (afmt != MOE_A_BF16) {
+    if (a->a1_codes) {
+      a1 = a->a1_codes;
+      a1s = a->a1_scales;
+    } else {
+      a1 = ws + L.a1_codes_off;
+      a1s = ws + L.a1_scales_off;
+      e = moe::launch_quant_act(a->hidden_states, a->T, a->H, afmt, nullptr, ws + L.a1_codes_off,
+                                ws + L.a1_scales_off, stream);
+      if (e != hipSuccess) return hip_status(e, "moe_experts_forward: a1 quantisation");
+    }
+  }
+  moe::GemmParams p{};
+  p.T = a->T;
+  p.slots_per_token = a->K;
+  p.sorted_slots = a->sorted_slots;
+  p.block_expert = a->block_expert;
+  p.num_padded = a->num_padded;
+  p.num_blocks = (int)(cap / a->block_m);
+  p.topk_weights = a->topk_weights;
+
+  // stage 1: gate/up GEMM + SiLU-and-mul -> h (bf16, sorted rows)
+  p.a = a1;
+  p.a_scale = a1s;
+  p.a_gather = 1;
+  p.w = a->w1;
+  p.w_scale = a->w1_scale;
+  p.N = a->I;
+  p.K = a->H;
+  p.Nw = 2 * a->I;
+  p.h = h;
+  e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
+  if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
+
+  // a2: re-quantise h in the activation format
+  const void* a2 = h;
+  const void* a2s = nullptr;
+  if (afmt != MOE_A_BF16) {
+    e = moe::launch_quant_act(h, (int)cap, a->I, afmt, a->num_padded, ws + L.a2_codes_off, ws + L.a2_scales_off,
+                              stream);
+    if (e != hipSuccess) return hip_status(e, "moe_experts_forward: a2 quantisation");
+    a2 = ws + L.a2_codes_off;
+    a2s = ws + L.a2_scales_off;
+  }
+
+  // stage 2: down GEMM, weighted by topk_weights -> per-slot fp32 rows
+  float* ybuf = (float*)(ws + L.ybuf_off);
+  p.a = a2;
+  p.a_scale = a2s;
+  p.a_gather = 0;
+  p.w = a->w2;
+  p.w_scale = a->w2_scale;
+  p.N = a->H;
+  p.K = a->I;
+  p.Nw = a->H;
+  p.h = nullptr;
+  p.ybuf = ybuf;
+  e = moe::launch_gemm(2, (int)a->wfmt, afmt, a->block_m, p, stream);
+  if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 2");
+
+  // ordered top-k combine
+  e = moe::launch_combine(ybuf, a->topk_ids, a->T, a->K, a->H, a->E_total, a->out, stream);
+  return hip_status(e, "moe_experts_forward: combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal (non-ABI) declarations shared by the libmoe translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Activation formats (values match moe_afmt in include/moe.h).
+enum { kABf16 = 0, kAMxfp4 = 1, kAFp8G128 = 2, kAFp8Token = 3 };
+// Weight formats (values match moe_wfmt).
+enum { kWMxfp4 = 0, kWFp8Block = 1, kWFp8Channel = 2 };
+
+// One grouped-GEMM launch over the padded sorted rows.
+struct GemmParams {
+  // A operand: bf16 [rows, K] or quantised codes + scales (layouts of moe_afmt).
+  const void* a;
+  const void* a_scale;
+  int a_gather;        // 1: A row = token of the sorted slot (stage 1); 0: A row = sorted row (stage 2)
+  // Weights of all experts: [E, Nw, K] in the weight format; Nw = 2I (stage 1) or H (stage 2).
+  const uint8_t* w;
+  const void* w_scale;
+  int N;               // output columns: I (stage 1, gate/up pairs) or H (stage 2)
+  int K;               // reduction length: H (stage 1) or I (stage 2)
+  int Nw;              // weight rows per expert
+  int T, slots_per_token;
+  const int32_t* sorted_slots;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int num_blocks;      // grid rows: capacity / block_m
+  // stage 1 output: h bf16 [cap, I]
+  uint16_t* h;
+  // stage 2 output: ybuf fp32 [T*K, H] by slot id, weighted by topk_weights
+  float* ybuf;
+  const float* topk_weights;
+};
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
+                             float shared_w, int32_t* ids, float* weights, hipStream_t stream);
+hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
+// rows_dev (optional): device row count; rows at or past it are skipped.
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, const int32_t* rows_dev,
+                            uint8_t* codes, void* scales, hipStream_t stream);
+hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmParams& p, hipStream_t stream);
+hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, int T, int K, int H, int E_total,
+                          uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

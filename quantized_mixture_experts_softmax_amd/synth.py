@@ -3,12 +3,13 @@
 This module only draws random numbers in the shapes and dtypes of the workloads;
 it holds none of the layer's arithmetic (no routing, sorting, quantisation rule or
 GEMM).  The same bytes feed the HIP path and the CPU oracle.  bf16 activations
-come from fp32 normal draws through torch's bfloat16 cast, FP8 weight codes from a
-fixed inverse-CDF table built with torch's float8_e4m3fn cast; both are library
-conversions, not the layer's quantisers.
+come from fp32 normal draws through torch's bfloat16 cast (a library conversion,
+not the layer's arithmetic).  Weight codes are uniform random bytes: two uniform
+e2m1 nibbles per MXFP4 byte; FP8 bytes with the exponent field held in [4, 7].
 
 Each tensor has its own child generator of numpy's PCG64 (SeedSequence(seed)
-spawned six ways: x, logits, w1, w1 scales, w2, w2 scales), so a tensor's values
+spawned six ways: x, logits, w1, w1 scales, w2, w2 scales; weight codes spawn one
+child per expert), so a tensor's values
 do not depend on the shapes of the others, and activations/logits drawn for the
 largest token count give the smaller counts as prefixes.
 
@@ -26,6 +27,7 @@ channel):
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -81,22 +83,9 @@ WORKLOADS = {
                             T_sweep=(1, 16, 256, 4096)),
 }
 
-_FP8_STD = 112.0  # spread of the FP8 weight codes (448 / 4)
-_fp8_table = None
-
-
-def _fp8_code_table() -> np.ndarray:
-    """65536 e4m3fn codes at the quantiles of N(0, 112^2) clipped to +-448, so that
-    uniform 16-bit draws give roughly normal FP8 weight codes."""
-    global _fp8_table
-    if _fp8_table is None:
-        import torch
-        from scipy.special import ndtri
-
-        p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
-        v = np.clip(ndtri(p) * _FP8_STD, -448.0, 448.0).astype(np.float32)
-        _fp8_table = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
-    return _fp8_table
+_FP8_MAG_MASK = np.uint64(0xBFBFBFBFBFBFBFBF)  # clear exponent bit 3 (bit 6 of the byte)
+_FP8_MAG_SET = np.uint64(0x2020202020202020)   # set exponent bit 1 (bit 5): exponent field in [4, 7]
+_FP8_RMS = 0.85                                 # approx. rms of the resulting code values
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -136,19 +125,38 @@ def make_logits(w: Workload, T: int | None = None) -> np.ndarray:
     return (logp[None, :] + g).astype(np.float32)
 
 
-def _weight(w: Workload, N: int, K: int, rng_codes, rng_scales):
-    """One [E_total, N, K] weight tensor in the workload's format."""
+def _expert_codes(seq, shape, fp8: bool) -> np.ndarray:
+    """Uniform random bytes for one expert.  FP8: the e4m3 exponent field is held in
+    [4, 7], so codes are finite (no NaN) with |value| in [0.125, 1.875] and a random
+    sign, uniform over those 64 codes."""
+    a = np.random.default_rng(seq).integers(0, 256, shape, dtype=np.uint8)
+    if fp8:
+        v = a.reshape(-1).view(np.uint64)
+        v &= _FP8_MAG_MASK
+        v |= _FP8_MAG_SET
+    return a
+
+
+def _weight(w: Workload, N: int, K: int, seq_codes, rng_scales):
+    """One [E_total, N, K] weight tensor in the workload's format; one child generator
+    per expert, filled by a thread pool (the result does not depend on scheduling)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     E = w.E_total
-    if w.wfmt == W_MXFP4:
-        codes = rng_codes.integers(0, 256, (E, N, K // 2), dtype=np.uint8)   # two uniform nibbles per byte
+    fp8 = w.wfmt != W_MXFP4
+    kb = K if fp8 else K // 2
+    codes = np.empty((E, N, kb), np.uint8)
+    seqs = seq_codes.spawn(E)
+
+    def fill(e):
+        codes[e] = _expert_codes(seqs[e], (N, kb), fp8)
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(E)))
+    if not fp8:
         scales = rng_scales.integers(118, 127, (E, N, K // 32), dtype=np.uint8)  # E8M0 exponent in [118, 126]
         return codes, scales
-    table = _fp8_code_table()
-    codes = np.empty((E, N, K), np.uint8)
-    for e in range(E):
-        idx = rng_codes.integers(0, 65536, (N, K), dtype=np.uint16)
-        codes[e] = table[idx]
-    base = 1.0 / (_FP8_STD * math.sqrt(K))
+    base = 1.0 / (_FP8_RMS * math.sqrt(K))
     if w.wfmt == W_FP8_BLOCK128:
         scales = (rng_scales.uniform(0.75, 1.25, (E, (N + 127) // 128, (K + 127) // 128)) * base).astype(np.float32)
     else:
@@ -158,9 +166,10 @@ def _weight(w: Workload, N: int, K: int, rng_codes, rng_scales):
 
 def make_weights(w: Workload):
     """(w1, w1_scale, w2, w2_scale) host arrays; w1 rows [0, I) gate, [I, 2I) up."""
+    seqs = np.random.SeedSequence(w.seed).spawn(6)
     r = _rngs(w.seed)
-    w1, w1s = _weight(w, 2 * w.I, w.H, r[2], r[3])
-    w2, w2s = _weight(w, w.H, w.I, r[4], r[5])
+    w1, w1s = _weight(w, 2 * w.I, w.H, seqs[2], r[3])
+    w2, w2s = _weight(w, w.H, w.I, seqs[4], r[5])
     return w1, w1s, w2, w2s
 
 

@@ -1,0 +1,130 @@
+"""Helpers of the GPU parity tests: move synthetic inputs to the device, run the
+HIP path through the C-ABI binding, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import oracle as orc
+from quantized_mixture_experts_softmax_amd import binding as B
+from quantized_mixture_experts_softmax_amd import synth
+
+DEV = "cuda:0"
+
+# Output bound on floating point results (max abs error relative to the oracle's rms,
+# and relative L2 error per token row).
+MAX_ABS_REL_RMS = 2e-2
+ROW_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def layer_for(w: synth.Workload, data: dict) -> orc.Layer:
+    return orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
+                     data["w2_scale"])
+
+
+def dev_weights(data: dict) -> dict:
+    return {k: to_dev(data[k]) for k in ("w1", "w1_scale", "w2", "w2_scale")}
+
+
+def score_name(w: synth.Workload) -> str:
+    return "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid"
+
+
+def combine_f32(res: dict, tokens: np.ndarray, K: int, H: int, E_total: int) -> np.ndarray:
+    """The GPU's fp32 result before its final bf16 rounding, rebuilt from the weighted
+    per-slot rows it left in the workspace by summing them in the combine kernel's
+    order (ascending slot, fp32)."""
+    ybuf = res["ybuf_dev"]
+    ids = res["ids"]
+    rows = (tokens[:, None] * K + np.arange(K)[None, :]).reshape(-1)
+    y = ybuf[torch.from_numpy(rows).to(ybuf.device)].cpu().numpy().reshape(len(tokens), K, H)
+    acc = np.zeros((len(tokens), H), np.float32)
+    for j in range(K):
+        ok = (ids[tokens, j] >= 0) & (ids[tokens, j] < E_total)
+        acc = np.where(ok[:, None], acc + y[:, j], acc).astype(np.float32)
+    return acc
+
+
+def check_rounding(got_bf16: np.ndarray, acc_f32: np.ndarray, what: str):
+    """The bf16 output is the round-to-nearest-even of the fp32 result, bit for bit."""
+    want = synth.f32_to_bf16_bits(acc_f32)
+    assert np.array_equal(got_bf16, want), f"{what}: bf16 output is not the rounded fp32 sum"
+
+
+def check_output(got, ref: np.ndarray, what: str, max_rel=MAX_ABS_REL_RMS, row_l2=ROW_REL_L2):
+    got = (synth.bf16_bits_to_f32(got) if got.dtype == np.uint16 else got).astype(np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    max_rel_err = float(err.max() / rms) if rms > 0 else float(err.max())
+    rn = np.sqrt(np.sum(ref ** 2, axis=1))
+    en = np.sqrt(np.sum((got - ref) ** 2, axis=1))
+    rows = en / np.maximum(rn, 1e-300)
+    say(f"{what}: max|d|/rms={max_rel_err:.3e} worst row rel L2={rows.max():.3e} rms={rms:.4g}")
+    assert max_rel_err <= max_rel, f"{what}: max|gpu-oracle| = {max_rel_err:.3e} * rms > {max_rel}"
+    assert rows.max() <= row_l2, f"{what}: row relative L2 {rows.max():.3e} > {row_l2}"
+    return max_rel_err, float(rows.max())
+
+
+def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dict | None = None):
+    """Route, sort, quantise and run the expert layer on the GPU through the ABI.
+    Returns a dict of host copies of every intermediate."""
+    wd = wd or dev_weights(data)
+    x = bf16_dev(data["x"])
+    logits = to_dev(data["logits"])
+    layer = B.MoELayer(wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], H=w.H, I=w.I, E=w.E, topk=w.topk,
+                       wfmt=w.wfmt, afmt=w.afmt, score=score_name(w), n_shared=w.n_shared,
+                       shared_weight=w.shared_weight, block_m=block_m)
+    out = layer(x, logits)
+    torch.cuda.synchronize()
+    b = layer._bufs[(x.shape[0], str(x.device))]
+    res = dict(out=bf16_host(out), ids=b["ids"].cpu().numpy(), weights=b["w"].cpu().numpy(), bm=b["bm"],
+               sort={k: v.cpu().numpy() for k, v in b["sort"].items()}, layer=layer, bufs=b)
+    if b["workspace"] is not None:
+        args = B.forward_args(x, wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], b["ids"], b["w"], b["sort"],
+                              w.wfmt, w.afmt, b["bm"], w.E_total, w.I, b["out"], b["workspace"],
+                              *(b["a1"] if b["a1"] else (None, None)))
+        L = B.moe_workspace_layout(args)
+        ws = b["workspace"]
+        cap = B.moe_sort_capacity(x.shape[0], w.K, w.E_total, b["bm"])
+        res["h_sorted"] = ws[L["h_off"]:L["h_off"] + L["h_bytes"]].cpu().numpy().view(np.uint16).reshape(cap, w.I)
+        if w.afmt != synth.A_BF16:
+            res["a2_codes"] = ws[L["a2_codes_off"]:L["a2_codes_off"] + L["a2_codes_bytes"]].cpu().numpy()
+            res["a2_scales"] = ws[L["a2_scales_off"]:L["a2_scales_off"] + L["a2_scales_bytes"]].cpu().numpy()
+            res["a1_codes"] = b["a1"][0].cpu().numpy()
+            res["a1_scales"] = b["a1"][1].cpu().numpy()
+        res["cap"] = cap
+        res["ybuf_dev"] = ws[L["ybuf_off"]:L["ybuf_off"] + L["ybuf_bytes"]].view(torch.float32).view(-1, w.H)
+    return res
+
+
+def h_by_slot(res: dict, T: int, K: int, I: int) -> np.ndarray:
+    """GPU stage-1 output rearranged from sorted rows to slot order [T*K, I]."""
+    ss = res["sort"]["sorted_slots"]
+    h = np.zeros((T * K, I), np.uint16)
+    valid = ss < T * K
+    h[ss[valid]] = res["h_sorted"][:len(ss)][valid]
+    return h

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects bad arguments on the host before touching the GPU (no GPU needed: only
+validation paths run here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_mixture_experts_softmax_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe.so is not built; run __graft_entry__.build()")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"moe_route_topk", "moe_align_sort", "moe_quant_act", "moe_experts_forward"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED) == names
+
+
+FAKE = 0x100000  # a 256-byte aligned non-null pointer that validation never dereferences
+
+
+def test_route_rejects(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_route_topk(P(FAKE), 4, 0, 1, 0, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_route_topk(P(FAKE), 4, 8, 9, 0, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_route_topk(P(FAKE), 4, 8, 2, 7, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_route_topk(None, 4, 8, 2, 0, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert "NULL" in B.moe_last_error()
+    assert lib.moe_route_topk(P(FAKE), 4, 2048, 2, 0, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+
+
+def test_sort_rejects(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_align_sort(P(FAKE), 4, 2, 8, 48, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert "block_m" in B.moe_last_error()
+    assert lib.moe_align_sort(P(FAKE), 4, 2, 2000, 16, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_align_sort(P(FAKE), 4, 2, 8, 16, None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert B.moe_sort_capacity(64, 4, 32, 16) == 64 * 4 + 32 * 15
+
+
+def test_quant_rejects(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_quant_act(P(FAKE), 4, 100, B.A_FP8_G128, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_quant_act(P(FAKE), 4, 128, B.A_BF16, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_quant_act(P(FAKE + 1), 4, 128, B.A_FP8_G128, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+
+
+def _args(**kw):
+    a = B.ForwardArgs()
+    a.T, a.H, a.I, a.E_total, a.K, a.block_m = 64, 256, 256, 8, 2, 16
+    a.wfmt, a.afmt, a.act = B.W_MXFP4, B.A_BF16, B.ACT_SILU
+    for f in ("hidden_states", "w1", "w1_scale", "w2", "w2_scale", "topk_ids", "topk_weights", "sorted_slots",
+              "block_expert", "num_padded", "out", "workspace"):
+        setattr(a, f, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_forward_rejects(lib):
+    fwd = lambda a: lib.moe_experts_forward(ctypes.byref(a), None)
+    assert fwd(_args(H=100)) == B.MOE_EINVAL
+    assert fwd(_args(block_m=8)) == B.MOE_EINVAL
+    assert fwd(_args(wfmt=B.W_FP8_BLOCK128, afmt=B.A_FP8_TOKEN)) == B.MOE_EUNSUPPORTED
+    assert fwd(_args(act=3)) == B.MOE_EUNSUPPORTED
+    assert fwd(_args(workspace_bytes=16)) == B.MOE_EWORKSPACE
+    assert "workspace" in B.moe_last_error()
+    assert fwd(_args(w1=None, workspace_bytes=1 << 40)) == B.MOE_EINVAL
+    assert fwd(_args(hidden_states=FAKE + 8, workspace_bytes=1 << 40)) == B.MOE_EINVAL
+    assert lib.moe_supports(B.W_MXFP4, B.A_MXFP4_G32, 0, 2880, 2880) == B.MOE_OK
+    assert lib.moe_supports(B.W_FP8_CHANNEL, B.A_FP8_G128, 0, 4096, 14336) == B.MOE_EUNSUPPORTED
+
+
+def test_workspace_layout(lib):
+    a = _args(T=64, H=2880, I=2880, E_total=32, K=4, block_m=16)
+    L = B.moe_workspace_layout(a)
+    cap = 64 * 4 + 32 * 15
+    assert L["h_bytes"] == cap * 2880 * 2 and L["ybuf_bytes"] == 64 * 4 * 2880 * 4
+    assert L["a2_codes_bytes"] == 0 and L["total"] == B.moe_experts_workspace_bytes(a)
+    for k, v in L.items():
+        if k.endswith("_off"):
+            assert v % 256 == 0
+    q = B.moe_workspace_layout(_args(T=64, H=7168, I=2048, E_total=257, K=9, block_m=128, wfmt=B.W_FP8_BLOCK128,
+                                     afmt=B.A_FP8_G128))
+    assert q["a1_scales_bytes"] == 64 * 56 * 4 and q["a2_codes_bytes"] > 0
+
+
+def test_pick_block_m(lib):
+    assert B.moe_pick_block_m(64, 4, 32) == 16
+    assert B.moe_pick_block_m(8192, 4, 128) == 128
+    assert B.moe_pick_block_m(256, 2, 8) == 64

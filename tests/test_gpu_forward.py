@@ -1,0 +1,202 @@
+"""GPU parity of the full expert layer (route -> sort -> quantise -> stage 1 ->
+stage 2 -> combine) against the oracle.
+
+Output bound: max|gpu - oracle| <= 2e-2 * rms(oracle) and per-token relative L2 <=
+1e-2, on the GPU's fp32 result before its final rounding to bf16 (rebuilt exactly
+from the per-slot fp32 rows in the workspace); the bf16 output is separately checked
+to be that result rounded to nearest even, bit for bit.  The bound is not applied to
+the bf16 values themselves because half a bf16 ulp of the largest outputs (up to ~9x
+rms on these workloads) already exceeds 2e-2 * rms.  Stage-1 h is checked element-wise to one bf16 ulp: both
+sides round an accumulated value to bf16 and the GPU's fp32 MFMA sum runs in another
+order than the oracle's fp64 sum.  For quantised activations that one-ulp freedom can
+move an h value across an a2 rounding boundary, and a single FP4 code step is a large
+change, so those paths are checked in stages: the GPU's a2 codes bit-exactly against
+the oracle quantiser applied to the GPU's own h, and the output bound against the
+oracle's stage 2 fed the GPU's h; the end-to-end result is reported with the count of
+differing a2 codes, which must stay below 0.2%, and a per-row L2 bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (B, DEV, bf16_dev, check_output, check_rounding, combine_f32, dev_weights, h_by_slot,
+                        layer_for, orc, run_layer, say, synth, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+W4A16 = (synth.W_MXFP4, synth.A_BF16)
+W4A4 = (synth.W_MXFP4, synth.A_MXFP4_G32)
+FP8B = (synth.W_FP8_BLOCK128, synth.A_FP8_G128)
+FP8C = (synth.W_FP8_CHANNEL, synth.A_FP8_TOKEN)
+
+
+def small(fmt, T=40, H=320, I=288, E=6, k=2, n_shared=0, score=synth.SCORE_SOFTMAX, seed=11):
+    return synth.Workload(f"small-{fmt[0]}-{fmt[1]}", T, H, I, E, k, fmt[0], fmt[1], score=score,
+                          n_shared=n_shared, seed=seed)
+
+
+def check_a2(res, w, what):
+    """GPU a2 codes and scales equal the oracle quantiser applied to the GPU's own h."""
+    npad = int(res["sort"]["num_padded"][0])
+    h = np.ascontiguousarray(res["h_sorted"][:npad])
+    rc, rs = orc.quant_act(h, w.afmt)
+    cs, ss, sdt = B.quant_shapes(w.afmt, res["cap"], w.I)
+    gc = res["a2_codes"].reshape(cs)[:npad]
+    gs = res["a2_scales"].view(np.uint8 if sdt == torch.uint8 else np.float32).reshape(ss)[:npad]
+    assert np.array_equal(gc, rc), f"{what}: a2 codes differ at {np.argwhere(gc != rc)[:5]}"
+    assert np.array_equal(gs.view(np.uint8), rs.view(np.uint8)), f"{what}: a2 scales differ"
+    say(f"{what}: a2 codes/scales bit-exact on {npad} sorted rows")
+
+
+def check_h_rows(h_gpu, ref_h, what):
+    """Stage-1 h: both sides round an accumulated value to bf16, so they may differ by
+    one bf16 ulp (<= 2^-7 relative) plus the fp32 accumulation error of the GPU sum."""
+    got = synth.bf16_bits_to_f32(h_gpu).astype(np.float64)
+    ref = synth.bf16_bits_to_f32(ref_h).astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bound = 2.0 ** -7 * np.maximum(np.abs(ref), np.abs(got)) + 1e-3 * rms
+    bad = np.abs(got - ref) > bound
+    rows = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    ulp_flips = int(np.count_nonzero(h_gpu != ref_h))
+    say(f"{what}: stage-1 h differs in {ulp_flips}/{h_gpu.size} values, worst row rel L2={rows.max():.3e}")
+    assert not bad.any(), f"{what}: stage-1 h outside one bf16 ulp at {np.argwhere(bad)[:5]}"
+    assert rows.max() <= 1e-2
+
+
+def full_check(w, data, res, tokens=None, what=""):
+    """Parity of one GPU run against the oracle on the listed tokens.
+    bf16 activations: the end-to-end output meets the output bound.
+    Quantised activations: a2 codes are bit-exact given the GPU's h, the output meets
+    the bound against the oracle's stage 2 fed the GPU's h, and the end-to-end result
+    (where a2 codes may differ because h was rounded differently) is reported with
+    the number of a2 codes that differ, which must stay a small fraction."""
+    L = layer_for(w, data)
+    ids, wts = res["ids"], res["weights"]
+    ref_ids, ref_w = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
+    assert np.array_equal(ids, ref_ids), f"{what}: topk_ids"
+    np.testing.assert_allclose(wts, ref_w, rtol=2e-6)
+    tk = np.arange(w.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    ref_h = orc.stage1(L, data["x"], ids, tk)
+    h_gpu = np.ascontiguousarray(h_by_slot(res, w.T, w.K, w.I).reshape(w.T, w.K, w.I)[tk].reshape(-1, w.I))
+    check_h_rows(h_gpu, ref_h, what)
+    ref = orc.stage2(L, ref_h, ids, wts, tk, T=w.T)  # == orc.forward on these tokens
+    acc = combine_f32(res, tk, w.K, w.H, w.E_total)
+    check_rounding(res["out"][tk], acc, what)
+    if w.afmt == synth.A_BF16:
+        return check_output(acc, ref, f"{what} end-to-end")
+    check_a2(res, w, what)
+    out2 = orc.stage2(L, h_gpu, ids, wts, tk, T=w.T)
+    check_output(acc, out2, f"{what} stage 2 on GPU h")
+    # a2 codes of the oracle's own h vs the GPU's h on the same slots
+    valid = ids[tk].reshape(-1) < w.E_total
+    c_ref, _ = orc.quant_act(ref_h[valid], w.afmt)
+    c_gpu, _ = orc.quant_act(h_gpu[valid], w.afmt)
+    flips = int(np.count_nonzero(c_ref != c_gpu))
+    e2e = check_output(acc, ref, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)",
+                       max_rel=0.1, row_l2=1e-2)
+    assert flips <= max(4, c_ref.size // 500), f"{what}: {flips} a2 code bytes differ"
+    return e2e
+
+
+SMALL = []
+for fmt in (W4A16, W4A4, FP8B, FP8C):
+    for bm in (16, 32, 64, 128):
+        SMALL.append((fmt, bm))
+
+
+@pytest.mark.parametrize("fmt,bm", SMALL, ids=[f"w{f[0]}a{f[1]}-bm{bm}" for f, bm in SMALL])
+def test_small_all_formats(fmt, bm):
+    # several K chunks with a ragged tail (H=320, I=288), ragged column strips, pad rows
+    if fmt == FP8B:
+        w = small(fmt, T=40, H=352, I=288, E=5, k=3, n_shared=1, score=synth.SCORE_SIGMOID)
+    elif fmt == FP8C:
+        w = small(fmt, T=33, H=320, I=416, E=4, k=2)
+    else:
+        w = small(fmt)
+    say(f"small forward {w.name} bm={bm} T={w.T} H={w.H} I={w.I} E={w.E_total} K={w.K}")
+    data = synth.make_all(w)
+    res = run_layer(w, data, block_m=bm)
+    full_check(w, data, res, what=f"{w.name}/bm{bm}")
+
+
+def test_determinism_and_token_permutation():
+    w = small(W4A16, T=48, E=5, k=2)
+    data = synth.make_all(w)
+    r1 = run_layer(w, data, block_m=16)
+    r2 = run_layer(w, data, block_m=16)
+    assert np.array_equal(r1["out"], r2["out"])
+    p = np.random.default_rng(0).permutation(w.T)
+    dp = dict(data, x=np.ascontiguousarray(data["x"][p]), logits=np.ascontiguousarray(data["logits"][p]))
+    r3 = run_layer(w, dp, block_m=16)
+    assert np.array_equal(r3["out"], r1["out"][p])
+
+
+def test_empty_tokens():
+    w = small(W4A16, T=0)
+    data = synth.make_all(w)
+    res = run_layer(w, data, block_m=16)
+    assert res["out"].shape == (0, w.H)
+
+
+def test_single_token_all_slots_one_expert():
+    w = small(W4A16, T=1, E=4, k=2)
+    data = synth.make_all(w)
+    res = run_layer(w, data, block_m=16)
+    full_check(w, data, res, what="single-token")
+
+
+# ---------------------------------------------------------------- full-size workloads
+def _sample(T, n, seed):
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,n_tok", [("tiny", 64), ("decode", 64), ("prefill", 24)])
+def test_full_size_mxfp4_w4a16(name, n_tok):
+    w = synth.WORKLOADS[name]
+    say(f"full-size {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.topk}")
+    data = synth.make_all(w)
+    res = run_layer(w, data)  # launch configuration of the benchmark (library-picked block_m)
+    full_check(w, data, res, tokens=_sample(w.T, n_tok, 5), what=name)
+
+
+def test_full_size_prefill_w4a4():
+    w = synth.WORKLOADS["prefill-w4a4"]
+    say(f"full-size {w.name}: T={w.T}")
+    data = synth.make_all(w)
+    res = run_layer(w, data)
+    # a1 codes are an integer product of the GPU quantiser: bit-exact on every token
+    rc, rs = orc.quant_act(data["x"], w.afmt)
+    assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
+    full_check(w, data, res, tokens=_sample(w.T, 24, 6), what=w.name)
+
+
+def test_full_size_fp8_block_shared():
+    w = synth.WORKLOADS["fp8-block"]
+    say(f"full-size {w.name}: T={w.T} H={w.H} I={w.I} E={w.E}+{w.n_shared}")
+    data = synth.make_all(w)
+    res = run_layer(w, data)
+    rc, rs = orc.quant_act(data["x"], w.afmt)
+    assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
+    assert np.all(res["ids"][:, w.topk] == w.E) and np.all(res["weights"][:, w.topk] == 1.0)
+    full_check(w, data, res, tokens=_sample(w.T, 6, 7), what=w.name)
+
+
+@pytest.fixture(scope="module")
+def fp8_channel_data():
+    w = synth.WORKLOADS["fp8-channel"]
+    return w, synth.make_all(w)
+
+
+@pytest.mark.parametrize("T", [1, 16, 256, 4096])
+def test_full_size_fp8_channel_sweep(fp8_channel_data, T):
+    w0, d0 = fp8_channel_data
+    w = w0.with_T(T)
+    say(f"full-size {w.name}: T={T}")
+    data = dict(d0, x=np.ascontiguousarray(d0["x"][:T]), logits=np.ascontiguousarray(d0["logits"][:T]))
+    res = run_layer(w, data)
+    rc, rs = orc.quant_act(data["x"], w.afmt)
+    assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
+    full_check(w, data, res, tokens=_sample(T, 6, 8), what=f"{w.name}/T{T}")

@@ -1,0 +1,120 @@
+"""GPU parity of the router, the align-sort and the activation quantisers against
+the oracle: bit-exact ids, counts, offsets, sorted slots, block owners, codes and
+scales; router weights within fp32 rounding of the oracle's fp64 values."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import DEV, B, bf16_dev, orc, say, synth, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ROUTER_CASES = [
+    # name, T, E, topk, score, renorm, n_shared, logits
+    ("tiny", 64, 8, 2, "softmax", True, 0, "normal"),
+    ("decode", 64, 32, 4, "softmax", True, 0, "normal15"),
+    ("prefill-zipf", 8192, 128, 4, "softmax", True, 0, "zipf"),
+    ("fp8-block", 4096, 256, 8, "sigmoid", True, 1, "normal"),
+    ("fp8-channel", 4096, 8, 2, "softmax", True, 0, "normal"),
+    ("ties", 300, 64, 6, "softmax", True, 0, "ties"),
+    ("no-renorm", 100, 96, 3, "softmax", False, 2, "normal"),
+    ("sigmoid-no-renorm", 100, 20, 5, "sigmoid", False, 0, "normal"),
+    ("max-E", 37, 1024, 32, "softmax", True, 32, "normal"),
+    ("top1", 50, 16, 1, "softmax", True, 0, "normal"),
+    ("single-token", 1, 8, 2, "softmax", True, 0, "normal"),
+]
+
+
+def make_logits(T, E, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "zipf":
+        w = synth.WORKLOADS["prefill"].scaled(T=T)
+        return synth.make_logits(w)
+    if kind == "ties":
+        return (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    std = 1.5 if kind == "normal15" else 1.0
+    return rng.normal(0, std, (T, E)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES, ids=[c[0] for c in ROUTER_CASES])
+def test_route_topk(case):
+    name, T, E, k, score, renorm, ns, kind = case
+    say(f"route {name}: T={T} E={E} k={k} {score} renorm={renorm} shared={ns}")
+    logits = make_logits(T, E, kind, 100 + T + E)
+    ids, w = B.moe_route_topk(to_dev(logits), k, score, renorm, ns, 0.5 if ns else 1.0)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = orc.route_topk(logits, k, orc.SCORE_SOFTMAX if score == "softmax" else orc.SCORE_SIGMOID,
+                                    renorm, ns, 0.5 if ns else 1.0)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-30)
+
+
+def test_route_empty():
+    ids, w = B.moe_route_topk(torch.empty((0, 8), dtype=torch.float32, device=DEV), 2)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 2)
+
+
+SORT_CASES = [(64, 2, 8, 16), (64, 4, 32, 16), (64, 4, 32, 32), (8192, 4, 128, 128), (8192, 4, 128, 64),
+              (4096, 9, 257, 128), (1, 2, 8, 16), (16, 2, 8, 16), (256, 2, 8, 64), (4096, 2, 8, 128),
+              (1000, 5, 1024, 16), (0, 4, 32, 16), (20000, 3, 7, 32)]
+
+
+@pytest.mark.parametrize("T,K,E,bm", SORT_CASES)
+def test_align_sort(T, K, E, bm):
+    say(f"align_sort T={T} K={K} E={E} bm={bm}")
+    rng = np.random.default_rng(T * 7 + K + E + bm)
+    if T >= 8192:  # Zipf-skewed ids from the router
+        logits = synth.make_logits(synth.WORKLOADS["prefill"].scaled(T=T, E=E))
+        ids, _ = orc.route_topk(logits, K)
+    else:
+        ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    got = B.moe_align_sort(to_dev(ids), E, bm)
+    torch.cuda.synchronize()
+    ref = orc.align_sort(ids, E, bm)
+    for key in ("expert_counts", "expert_offsets", "sorted_slots"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    nb = len(ref["block_expert"])
+    assert np.array_equal(got["block_expert"].cpu().numpy()[:nb], ref["block_expert"])
+    assert int(got["num_padded"].cpu()[0]) == ref["num_padded"]
+
+
+def test_align_sort_invalid_ids_dropped():
+    ids = np.array([[0, 5], [9, -1], [2, 2], [5, 5]], np.int32)
+    got = B.moe_align_sort(to_dev(ids), 6, 16)
+    torch.cuda.synchronize()
+    ref = orc.align_sort(ids, 6, 16)
+    for key in ("expert_counts", "expert_offsets", "sorted_slots"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+
+
+QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8_G128, 33, 160),
+               ("fp8-token", B.A_FP8_TOKEN, 40, 4096), ("fp8-token-wide", B.A_FP8_TOKEN, 3, 14336),
+               ("mxfp4", B.A_MXFP4_G32, 40, 2880), ("mxfp4-small", B.A_MXFP4_G32, 1, 32)]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_quant_act(case):
+    name, fmt, rows, cols = case
+    say(f"quant {name} rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * cols)
+    scale = np.exp(rng.uniform(-8, 8, (rows, 1)))
+    xf = rng.standard_normal((rows, cols)) * scale
+    xf[0, :] = 0.0                      # all-zero row
+    if rows > 2:
+        xf[1, ::7] = -0.0
+        xf[2, :] = np.round(xf[2, :] * 4) / 4  # many exact grid points / ties
+    x = synth.f32_to_bf16_bits(xf.astype(np.float32))
+    codes, scales = B.moe_quant_act(bf16_dev(x), fmt)
+    torch.cuda.synchronize()
+    rc, rs = orc.quant_act(x, fmt)
+    gc = codes.cpu().numpy()
+    gs = scales.cpu().numpy()
+    assert np.array_equal(gs.view(np.uint8) if gs.dtype != np.uint8 else gs, rs.view(np.uint8)), "scales"
+    assert np.array_equal(gc, rc), f"codes differ at {np.argwhere(gc != rc)[:5]}"
+
+
+def test_quant_act_empty():
+    codes, scales = B.moe_quant_act(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), B.A_FP8_G128)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 64)
