@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE expert layer hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch already resident in HBM:
+moe_route_topk -> moe_align_sort -> (moe_quant_act for quantised activations) ->
+moe_experts_forward (stage-1 GEMM + SiLU-and-mul, a2 quantisation, stage-2 GEMM
+weighted by the top-k weights, ordered combine).  Every step reads a different copy of
+the weights when one copy would fit twice in the 256 MB Infinity Cache, so weight
+bytes come from HBM.
+
+Default workload: the decode-shaped MXFP4 w4a16 layer (T=64, H=I=2880, E=32, top-4),
+with the weights in the tiled kernel layout (moe_tile_weights, a one-time permutation
+done when the weights are loaded, outside the timed region).
+
+Prints ONE JSON line.  `roofline` is for the stage-1 GEMM (the dominant kernel): its
+algorithmic bytes (or flops) per launch divided by its average duration, timed with HIP
+events recorded on the launch stream around every stage-1 launch of the timed steps.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE layer tokens/s; % HBM peak (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def _event(hip):
+    e = ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    return e.value
+
+
+def _elapsed_ms(hip, a, b) -> float:
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def algorithmic(w, ids_np):
+    """Algorithmic bytes and flops of one step and of its stage-1 GEMM launch.
+    Weights count once per expert that at least one slot uses; rows are the routed
+    slots (pad rows are overhead, not work)."""
+    import numpy as np
+
+    from quantized_mixture_experts_softmax_amd import synth
+
+    hit = np.unique(ids_np[(ids_np >= 0) & (ids_np < w.E_total)])
+    n_hit = len(hit)
+    slots = int(np.count_nonzero((ids_np >= 0) & (ids_np < w.E_total)))
+    if w.wfmt == synth.W_MXFP4:
+        w1_per = 2 * w.I * (w.H // 2 + w.H // 32)
+        w2_per = w.H * (w.I // 2 + w.I // 32)
+    elif w.wfmt == synth.W_FP8_BLOCK128:
+        w1_per = 2 * w.I * w.H + 4 * ((2 * w.I + 127) // 128) * ((w.H + 127) // 128)
+        w2_per = w.H * w.I + 4 * ((w.H + 127) // 128) * ((w.I + 127) // 128)
+    else:
+        w1_per = 2 * w.I * w.H + 4 * 2 * w.I
+        w2_per = w.H * w.I + 4 * w.H
+    x_bytes = w.T * w.H * 2
+    out_bytes = w.T * w.H * 2
+    h_bytes = slots * w.I * 2
+    step_bytes = n_hit * (w1_per + w2_per) + x_bytes + out_bytes
+    gemm1_bytes = n_hit * w1_per + x_bytes + h_bytes
+    gemm1_flops = 2.0 * slots * w.H * 2 * w.I
+    step_flops = 6.0 * slots * w.H * w.I
+    return dict(n_hit=n_hit, slots=slots, step_bytes=step_bytes, gemm1_bytes=gemm1_bytes, gemm1_flops=gemm1_flops,
+                step_flops=step_flops)
+
+
+def mfma_dtype(w):
+    from quantized_mixture_experts_softmax_amd import synth
+
+    if w.wfmt == synth.W_MXFP4:
+        return "fp4" if w.afmt == synth.A_MXFP4_G32 else "bf16"
+    return "fp8"
+
+
+def traffic_from_profiles(workload_name: str):
+    """HBM bytes per stage-1 launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"gemm1_{workload_name}_pmc.txt")
+    src = os.path.join(ROOT, "quantized_mixture_experts_softmax_amd", "csrc", "experts_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in open(path):
+        if "=" in line and line.strip().startswith("TRAFFIC_"):
+            k, v = line.strip().split("=", 1)
+            vals[k] = v.strip()
+    if vals.get("TRAFFIC_SOURCE_SHA") != sha or "TRAFFIC_BYTES_PER_LAUNCH" not in vals:
+        return None
+    return float(vals["TRAFFIC_BYTES_PER_LAUNCH"])
+
+
+def cpu_baseline(w, data, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload (rank 0, N=1)."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    ids, wts = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
+    L = orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
+                  data["w2_scale"])
+    per_call = max(1, min(w.T, 64))
+    done, t0, start = 0, time.perf_counter(), 0
+    while True:
+        tk = (np.arange(per_call) + start) % w.T
+        orc.forward(L, data["x"], ids, wts, tk.astype(np.int32))
+        done += per_call
+        start += per_call
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{done} tokens of the {w.name} workload ({per_call} per call), oracle forward "
+                      f"(fp64 per-token loop, OpenMP), {el:.1f} s"}
+
+
+def main() -> int:
+    from quantized_mixture_experts_softmax_amd import synth
+
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=None, help="token count (fp8-channel sweep: 1, 16, 256, 4096)")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--weight-copies", type=int, default=None)
+    ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
+                    help="weight layout: the kernel layout prepared once by moe_tile_weights, or canonical")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU (expert/tensor parallel) path is "
+              "described in DESIGN.md and not implemented. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from quantized_mixture_experts_softmax_amd import binding as B
+
+    if not os.path.exists(B.LIB_PATH):
+        from quantized_mixture_experts_softmax_amd import build as hip_build
+
+        hip_build.build()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_T(args.tokens)
+    data = synth.make_all(w)
+    wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale"))
+    # enough copies that one rotation is larger than twice the Infinity Cache
+    copies = args.weight_copies or (1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    layers = []
+    for _ in range(copies):
+        layers.append(B.MoELayer(t(data["w1"]), t(data["w1_scale"]), t(data["w2"]), t(data["w2_scale"]), H=w.H,
+                                 I=w.I, E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
+                                 score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
+                                 n_shared=w.n_shared, shared_weight=w.shared_weight, block_m=args.block_m,
+                                 tiled=args.layout == "tiled"))
+    x = torch.from_numpy(data["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = t(data["logits"])
+    hip = _hip()
+
+    for i in range(args.warmup):
+        layers[i % copies](x, logits)
+    torch.cuda.synchronize()
+    evs = [[_event(hip) for _ in range(4)] for _ in range(args.steps)]
+    ev_start, ev_stop = _event(hip), _event(hip)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    t0 = time.perf_counter()
+    hip.hipEventRecord(ctypes.c_void_p(ev_start), ctypes.c_void_p(stream))
+    for s in range(args.steps):
+        B.moe_profile_events(evs[s])
+        layers[s % copies](x, logits)
+    hip.hipEventRecord(ctypes.c_void_p(ev_stop), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.moe_profile_events(None)
+    gpu_ms = _elapsed_ms(hip, ev_start, ev_stop)
+    g1 = [_elapsed_ms(hip, e[0], e[1]) for e in evs]
+    g2 = [_elapsed_ms(hip, e[1], e[2]) for e in evs]
+    cb = [_elapsed_ms(hip, e[2], e[3]) for e in evs]
+
+    ms_per_step = wall * 1e3 / args.steps
+    b = layers[0]._bufs[(w.T, str(dev))]
+    ids_np = b["ids"].cpu().numpy()
+    alg = algorithmic(w, ids_np)
+    g1_ms = float(np.mean(g1))
+    dt = mfma_dtype(w)
+    t_hbm = alg["gemm1_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["gemm1_flops"] / (MFMA_PEAK_TFLOPS[dt] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = alg["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg["gemm1_flops"] / (g1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4)}
+    traffic = traffic_from_profiles(w.name if not args.tokens else f"{w.name}-T{w.T}")
+    roof["traffic"] = traffic
+    roof["kernel"] = "moe_gemm_kernel stage 1 (gate/up GEMM + SiLU-and-mul)"
+    roof["alg_bytes_per_launch"] = alg["gemm1_bytes"]
+    roof["alg_flops_per_launch"] = alg["gemm1_flops"]
+    roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded; random weight codes and scales, no checkpoint)",
+        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel'][w.wfmt]}-"
+                               f"{['w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token'][w.afmt]}",
+                   "T": w.T, "H": w.H, "I": w.I, "experts": w.E, "shared_experts": w.n_shared, "topk": w.topk,
+                   "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
+                   "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
+                   "weight_layout": args.layout},
+        "roofline": roof,
+        "step_breakdown_us": {"gpu_step": round(gpu_ms * 1e3 / args.steps, 2),
+                              "stage1_gemm": round(g1_ms * 1e3, 2), "a2_quant+stage2_gemm": round(float(np.mean(g2)) * 1e3, 2),
+                              "combine": round(float(np.mean(cb)) * 1e3, 2)},
+        "step_roofline": {"alg_bytes": alg["step_bytes"], "alg_flops": alg["step_flops"],
+                          "hbm_frac": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(alg["step_flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[dt], 4)},
+    }
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -65,6 +65,17 @@ typedef enum moe_wfmt { MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANN
  *   MOE_A_FP8_TOKEN  codes e4m3fn [rows, cols], scales fp32 [rows] */
 typedef enum moe_afmt { MOE_A_BF16 = 0, MOE_A_MXFP4_G32 = 1, MOE_A_FP8_G128 = 2, MOE_A_FP8_TOKEN = 3 } moe_afmt;
 
+/* Weight memory layout.
+ *   MOE_LAYOUT_CANONICAL  the row-major tensors described under moe_wfmt.
+ *   MOE_LAYOUT_TILED      the kernel layout written by moe_tile_weights: a one-time
+ *                         permutation of the same codes (and, for MXFP4, of the E8M0
+ *                         scales) into 16-row x 128-K blocks in the lane order of the MFMA
+ *                         operands, so every wavefront load is one contiguous 1 KB run.
+ *                         The pages shuffle expert weights into a kernel format once, after
+ *                         loading ([mxfp4.py] Mxfp4MoEMethod._setup_kernel,
+ *                         process_weights_after_loading); this is that step for this library. */
+typedef enum moe_weight_layout { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED = 1 } moe_weight_layout;
+
 /* Gated activation.  Only SiLU-and-mul: h = silu(gate) * up, silu(z) = z / (1 + e^-z)
  * ([rocm_aiter_moe] AiterExperts: SILU activation, act-and-mul only). */
 typedef enum moe_act { MOE_ACT_SILU = 0 } moe_act;
@@ -175,6 +186,7 @@ typedef struct moe_forward_args {
   uint16_t* out;                                 /* [T, H] bf16, written */
   void* workspace;
   size_t workspace_bytes;
+  moe_weight_layout weight_layout;               /* layout of w1 and w2 (both the same) */
 } moe_forward_args;
 
 /* Byte offsets into the workspace (each 256-byte aligned); 0 size = not used. */
@@ -190,6 +202,25 @@ size_t moe_experts_workspace_bytes(const moe_forward_args* a);
 moe_status moe_workspace_layout(const moe_forward_args* a, moe_workspace_layout_t* layout);
 moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * moe_tile_weights -- one-time permutation of one weight tensor ([E, N, K] codes in the
+ * canonical layout of `wfmt`, i.e. w1 with N = 2I, K = H or w2 with N = H, K = I) into
+ * MOE_LAYOUT_TILED.  Block (e, n16, c) holds rows [16*n16, 16*n16+16) and K elements
+ * [128c, 128c+128) (zero past K); lane l = 16*g + r of a wavefront owns row r, elements
+ * [128c + 32g, +32):
+ *   MXFP4: 1088 bytes per block = 64 lanes x 16 code bytes, then 64 E8M0 bytes (lane order);
+ *          w_scale must be the canonical [E, N, K/32] bytes and is folded into `out`
+ *          (forward calls on tiled MXFP4 weights ignore w1_scale / w2_scale).
+ *   FP8:   2048 bytes per block = 64 lanes x 16 bytes (elements 32g..32g+15), then
+ *          64 lanes x 16 bytes (32g+16..32g+31); scales stay in their canonical arrays and
+ *          are still passed to moe_experts_forward.
+ * Blocks are ordered [E][N/16][ceil(K/128)].  `out` holds moe_tiled_weight_bytes() bytes.
+ * Limits: N % 16 == 0, K % 32 == 0.  Device pointers; enqueued on `stream`.
+ * ---------------------------------------------------------------------------------- */
+size_t moe_tiled_weight_bytes(moe_wfmt wfmt, int E, int N, int K);
+moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w, const void* w_scale,
+                            uint8_t* out, hipStream_t stream);
+
 /* Whether a (wfmt, afmt, act, H, I) combination is implemented (MOE_OK) or not
  * (MOE_EUNSUPPORTED / MOE_EINVAL, with the reason in moe_last_error()); the analogue of
  * [rocm_aiter_moe] AiterExperts.is_supported_config. */
@@ -198,6 +229,13 @@ moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I)
 /* A row tile for moe_align_sort / moe_experts_forward suited to T*K slots over E_total
  * experts (host-side heuristic; any value in {16, 32, 64, 128} is valid). */
 int moe_pick_block_m(int T, int K, int E_total);
+
+/* Profiling hook.  While enabled (count == 4), moe_experts_forward calls made on this
+ * thread record, on their stream, events[0] just before the stage-1 GEMM, events[1] just
+ * after it, events[2] after the stage-2 GEMM and events[3] after the combine, so a caller
+ * can time the kernels inside a running pipeline.  count == 0 disables it.  The events are
+ * created and owned by the caller and must stay valid while enabled. */
+moe_status moe_profile_events(hipEvent_t* events, int count);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* moe_last_error(void);

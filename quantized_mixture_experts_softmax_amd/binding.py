@@ -23,8 +23,10 @@ ACT_SILU = 0
 EXPORTED = [
     "moe_route_topk", "moe_sort_capacity", "moe_align_sort", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
-    "moe_supports", "moe_pick_block_m", "moe_last_error",
+    "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
+    "moe_tiled_weight_bytes", "moe_tile_weights",
 ]
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -46,6 +48,7 @@ class ForwardArgs(ctypes.Structure):
         ("sorted_slots", ctypes.c_void_p), ("block_expert", ctypes.c_void_p), ("num_padded", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("weight_layout", ctypes.c_int),
     ]
 
 
@@ -85,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.moe_supports.argtypes = [I, I, I, I, I]
         L.moe_pick_block_m.restype = I
         L.moe_pick_block_m.argtypes = [I, I, I]
+        L.moe_profile_events.restype = S
+        L.moe_profile_events.argtypes = [P, I]
+        L.moe_tiled_weight_bytes.restype = ctypes.c_size_t
+        L.moe_tiled_weight_bytes.argtypes = [I, I, I, I]
+        L.moe_tile_weights.restype = S
+        L.moe_tile_weights.argtypes = [I, I, I, I, P, P, P, P]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         _lib = L
@@ -118,6 +127,28 @@ def _dev(t: torch.Tensor) -> torch.device:
 
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
+
+
+def moe_profile_events(events: list | None) -> None:
+    """Enable (4 raw hipEvent_t handles) or disable (None) the stage-boundary events."""
+    if not events:
+        _check(lib().moe_profile_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * 4)(*events)
+    _check(lib().moe_profile_events(arr, 4))
+
+
+def moe_tile_weights(w: torch.Tensor, w_scale: torch.Tensor | None, wfmt: int, K: int, stream=None) -> torch.Tensor:
+    """Tiled (kernel-layout) copy of one [E, N, K] weight tensor; see include/moe.h."""
+    dev = _dev(w)
+    E, N = w.shape[0], w.shape[1]
+    n = lib().moe_tiled_weight_bytes(wfmt, E, N, K)
+    if n == 0:
+        raise ValueError("moe_tiled_weight_bytes: unsupported shape")
+    out = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(lib().moe_tile_weights(wfmt, E, N, K, _ptr(w), _ptr(w_scale) if wfmt == W_MXFP4 else None, _ptr(out),
+                                  _stream(stream, dev)))
+    return out
 
 
 def moe_supports(wfmt: int, afmt: int, H: int, I: int, act: int = ACT_SILU) -> bool:
@@ -191,7 +222,7 @@ def moe_quant_act(x: torch.Tensor, fmt: int, codes=None, scales=None, stream=Non
 
 def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
                  afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
-                 a1_scales=None) -> ForwardArgs:
+                 a1_scales=None, weight_layout: int = LAYOUT_CANONICAL) -> ForwardArgs:
     T, H = hidden_states.shape
     K = topk_ids.shape[1]
     a = ForwardArgs()
@@ -206,6 +237,7 @@ def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weigh
     a.out = _ptr(out)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.weight_layout = weight_layout
     return a
 
 
@@ -224,7 +256,7 @@ def moe_workspace_layout(args: ForwardArgs) -> dict:
 
 def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
                         afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
-                        a1_scales=None, stream=None):
+                        a1_scales=None, stream=None, weight_layout: int = LAYOUT_CANONICAL):
     """Returns (out, workspace).  The workspace may be passed back in on later calls."""
     dev = _dev(hidden_states)
     assert hidden_states.dtype == torch.bfloat16
@@ -232,7 +264,7 @@ def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, top
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     args = forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort, wfmt, afmt,
-                        block_m, E_total, I, out, workspace, a1_codes, a1_scales)
+                        block_m, E_total, I, out, workspace, a1_codes, a1_scales, weight_layout)
     need = moe_experts_workspace_bytes(args)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -248,7 +280,15 @@ class MoELayer:
     step one libmoe call.  Buffers are allocated on first use and reused."""
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
-                 score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None):
+                 score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
+                 tiled: bool = False):
+        """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights)."""
+        self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
+        if tiled:
+            w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
+            w2 = moe_tile_weights(w2, w2_scale, wfmt, I)
+            if wfmt == W_MXFP4:
+                w1_scale = w2_scale = None
         self.w1, self.w1_scale, self.w2, self.w2_scale = w1, w1_scale, w2, w2_scale
         self.H, self.I, self.E, self.topk = H, I, E, topk
         self.wfmt, self.afmt, self.score = wfmt, afmt, score
@@ -293,5 +333,5 @@ class MoELayer:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
         out, b["workspace"] = moe_experts_forward(
             x, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"], self.wfmt, self.afmt,
-            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream)
+            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout)
         return out

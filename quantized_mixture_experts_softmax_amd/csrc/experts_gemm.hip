@@ -34,14 +34,59 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int kXcds = 8;
+
+// MFMA column tiles per wave of the small-block kernel.  bf16 activations cost as
+// many bytes per row as four MXFP4 weight rows, so that path takes wider strips to
+// amortise the activation reads over more weight rows.
+#ifndef MOE_KSPLIT_NT_BF16
+#define MOE_KSPLIT_NT_BF16 8
+#endif
+#ifndef MOE_KSPLIT_NT_Q
+#define MOE_KSPLIT_NT_Q 4
+#endif
+// Workgroups per CU the small-block launch is sized for (strips per workgroup grow
+// until the grid is about this many workgroups per CU).
+#ifndef MOE_KSPLIT_WGS_PER_CU
+#define MOE_KSPLIT_WGS_PER_CU 2
+#endif
 
 __device__ __forceinline__ int xcd_remap(int L, int G) {
   const int per = G / kXcds, rem = G % kXcds;
   const int x = L % kXcds, i = L / kXcds;
   return x * per + (x < rem ? x : rem) + i;
+}
+
+// Branch-free predicated loads: when the predicate is false the load reads this
+// all-zero array instead, so the compiler emits straight-line loads and never has to
+// wait for a load before the value is consumed (a guarded load becomes an exec-masked
+// branch that waits for every load in flight; a select on the loaded value waits for
+// that load).  Zero data contributes nothing to any MFMA product; a zero E8M0 scale
+// byte is the finite 2^-127.
+// Both candidate addresses are global memory; saying so keeps the loads global_load
+// (a generic pointer would make them flat loads, which the compiler must wait for
+// conservatively).  Nothing ever writes kZeroPage.
+__device__ __attribute__((aligned(64))) uint8_t kZeroPage[64];
+
+#define MOE_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* base, size_t off_bytes, bool ok) {
+  const MOE_GLOBAL uint8_t* zp = (const MOE_GLOBAL uint8_t*)kZeroPage;
+  const MOE_GLOBAL uint8_t* b = (const MOE_GLOBAL uint8_t*)base;
+  return *(const MOE_GLOBAL T*)(ok ? b + off_bytes : zp);
+}
+__device__ __forceinline__ i32x4 ld16(const uint8_t* base, size_t off, bool ok) {
+  return ld_global<i32x4>(base, off, ok);
+}
+__device__ __forceinline__ uint32_t ld8(const uint8_t* base, size_t off, bool ok) {
+  return ld_global<uint8_t>(base, off, ok);
+}
+__device__ __forceinline__ float ldf(const float* base, size_t off, bool ok) {
+  return ld_global<float>(base, off * sizeof(float), ok);
 }
 
 template <int WF, int NT>
@@ -51,8 +96,39 @@ struct WeightRegs {
   float sb[NT];                        // FP8 block: w_scale of this chunk
 };
 
-template <int STAGE, int WF, int AF, int BM, int NT>
+// Where a lane's weight bytes live.  WL = 0: canonical row-major [E][Nw][K*] codes and
+// [E][Nw][K/32] E8M0 scales; WL = 1: the tiled layout of moe_tile_weights, blocks of 16
+// rows x 128 K in MFMA lane order, [E][Nw/16][nch] blocks, MXFP4 scales inside the block.
+// `trow` is the first row of the lane's 16-row tile (tiles never straddle 16-row
+// boundaries: Nw, I and H are multiples of 16), li the lane's row inside it.
+template <int WF, int WL>
+struct WLayout {
+  static constexpr size_t kBlock = (WF == kWMxfp4) ? 1088 : 2048;
+  static constexpr size_t kDataStride = WL ? kBlock : ((WF == kWMxfp4) ? 64 : 128);  // per 128-K chunk
+  static constexpr size_t kScaleStride = WL ? kBlock : 4;
+  static constexpr size_t kHiOff = WL ? 1024 : 16;  // FP8: second 16 B piece of the lane
+  __device__ static const uint8_t* data(const GemmParams& p, int e, int trow, int li, int g, int lane, int K) {
+    if constexpr (WL) {
+      const size_t blk = ((size_t)e * p.Nw + trow) / 16 * (size_t)((K + 127) / 128);
+      return p.w + blk * kBlock + 16 * lane;
+    } else {
+      const size_t rowb = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
+      return p.w + ((size_t)e * p.Nw + trow + li) * rowb + (WF == kWMxfp4 ? 16 * g : 32 * g);
+    }
+  }
+  __device__ static const uint8_t* scale(const GemmParams& p, int e, int trow, int li, int g, int lane, int K) {
+    if constexpr (WL) {
+      const size_t blk = ((size_t)e * p.Nw + trow) / 16 * (size_t)((K + 127) / 128);
+      return p.w + blk * kBlock + 1024 + lane;
+    } else {
+      return (const uint8_t*)p.w_scale + ((size_t)e * p.Nw + trow + li) * (size_t)(K / 32) + g;
+    }
+  }
+};
+
+template <int STAGE, int WF, int AF, int BM, int NT, int WL>
 __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
+  using WLay = WLayout<WF, WL>;
   constexpr int ARB = (AF == kABf16) ? 256 : (AF == kAMxfp4 ? 64 : 128);  // A bytes per row per chunk
   constexpr int APC = ARB / 16;                                            // 16 B pieces per row per chunk
   constexpr int EPP = 128 / APC;                                           // elements per piece
@@ -131,41 +207,37 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
   bool col_ok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int c, wrow;
+    int c, trow;
     if (STAGE == 1) {
       const int tt = t % (NT / 2);
       c = nt_idx * COLS_PER_WG + w * (NT / 2) * 16 + tt * 16 + li;
       col_ok[t] = c < p.N;
-      wrow = col_ok[t] ? (t < NT / 2 ? c : p.N + c) : 0;
+      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
     } else {
       c = nt_idx * COLS_PER_WG + w * NT * 16 + t * 16 + li;
       col_ok[t] = c < p.N;
-      wrow = col_ok[t] ? c : 0;
+      trow = col_ok[t] ? c - li : 0;
     }
     col[t] = c;
-    const size_t rowi = (size_t)e * p.Nw + wrow;
-    w_src[t] = p.w + rowi * w_row_bytes + (WF == kWMxfp4 ? 16 * g : 32 * g);
-    ws_src[t] = (const uint8_t*)p.w_scale + rowi * (size_t)(K / 32) + g;
-    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + wrow / 128) * nbk;
-    wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[rowi] : 1.0f;
+    w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
+    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
+    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
+    wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + trow + li] : 1.0f;
   }
 
   auto load_a = [&](int c, i32x4 (&reg)[AIT]) {
 #pragma unroll
-    for (int it = 0; it < AIT; ++it) {
-      const bool ok = a_ok[it] && (c * 128 + a_k0[it] < K);
-      reg[it] = ok ? *(const i32x4*)(a_src[it] + (size_t)c * ARB) : i32x4{0, 0, 0, 0};
-    }
+    for (int it = 0; it < AIT; ++it)
+      reg[it] = ld16(a_src[it], (size_t)c * ARB, a_ok[it] && (c * 128 + a_k0[it] < K));
   };
   auto load_as = [&](int c, float& fs, uint32_t& qs) {
     if constexpr (AF == kAFp8G128) {
-      fs = s_ok ? ((const float*)p.a_scale)[(size_t)s_row * nch + c] : 0.0f;
+      fs = ldf((const float*)p.a_scale, (size_t)s_row * nch + c, s_ok);
     } else if constexpr (AF == kAMxfp4) {
       const uint8_t* sp = (const uint8_t*)p.a_scale + (size_t)s_row * (K / 32) + c * 4;
       uint32_t v = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (s_ok && c * 128 + 32 * q < K) v |= (uint32_t)sp[q] << (8 * q);
+      for (int q = 0; q < 4; ++q) v |= ld8(sp, q, s_ok && c * 128 + 32 * q < K) << (8 * q);
       qs = v;
     }
   };
@@ -183,11 +255,11 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (WF == kWMxfp4) {
-        r.w[t][0] = kok ? *(const i32x4*)(w_src[t] + (size_t)c * 64) : i32x4{0, 0, 0, 0};
-        r.s[t] = kok ? (uint32_t)ws_src[t][c * 4] : 127u;
+        r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
+        r.s[t] = ld8(ws_src[t], (size_t)c * WLay::kScaleStride, kok);
       } else {
-        r.w[t][0] = kok ? *(const i32x4*)(w_src[t] + (size_t)c * 128) : i32x4{0, 0, 0, 0};
-        r.w[t][WF == kWMxfp4 ? 0 : 1] = kok ? *(const i32x4*)(w_src[t] + (size_t)c * 128 + 16) : i32x4{0, 0, 0, 0};
+        r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
+        r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)c * WLay::kDataStride + WLay::kHiOff, kok);
         if constexpr (WF == kWFp8Block) r.sb[t] = wsb_src[t][c];
       }
     }
@@ -332,6 +404,540 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Small-block kernel (BM <= 32 rows, the decode shape).  With few rows per expert
+// the GEMM is a weight stream: every weight byte is used by at most BM rows, so the
+// kernel must keep HBM reads in flight all the time.  The four waves of a workgroup
+// share the output tiles of a column strip and split K between them (wave w takes
+// chunks w, w+4, w+8, ...); each wave loads its A fragments (L2-resident
+// activations) and weights straight into registers in MFMA operand layout, one
+// chunk ahead of the MFMAs, with no LDS staging and no barrier in the K loop.  One
+// workgroup walks `strips_per_wg` consecutive column strips of the same row block as
+// a single stream, so the prefetch runs across strip boundaries and the start-up
+// latency (block owner -> sorted slots -> rows) is paid once.  At the end of each
+// strip the four partial sums are added through LDS in fixed wave order
+// (deterministic; double-buffered, one barrier per strip) and wave 0 runs the
+// epilogue while the other waves stream on.
+template <int AF, int MT>
+struct ARegs {
+  i32x4 a[MT][AF == kABf16 ? 4 : (AF == kAMxfp4 ? 1 : 2)];  // 64 B / 16 B / 32 B per m-tile
+  uint32_t sa[MT];                                          // MXFP4: E8M0 byte of the lane's row/group
+  float as[MT][4];                                          // FP8 block: scales of the 4 output rows
+};
+
+template <int STAGE, int WF, int AF, int BM, int NT, int WL>
+__global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p) {
+  using WLay = WLayout<WF, WL>;
+  constexpr int MT = BM / 16;
+  constexpr int COLS_PER_STRIP = (STAGE == 1) ? 8 * NT : 16 * NT;
+  constexpr int NACC = MT * NT * 4;
+  constexpr int NA = (AF == kABf16) ? 4 : (AF == kAMxfp4 ? 1 : 2);
+  static_assert(STAGE == 2 || NT % 2 == 0, "stage 1 pairs gate and up tiles");
+  __shared__ float red[2][3][NACC][64];
+
+  const int n_strips = (p.N + COLS_PER_STRIP - 1) / COLS_PER_STRIP;
+  const int S = p.strips_per_wg;
+  const int n_groups = (n_strips + S - 1) / S;
+  const int G = p.num_blocks * n_groups;
+  const int lid = xcd_remap((int)blockIdx.x, G);
+  const int b = lid % p.num_blocks;
+  const int grp = lid / p.num_blocks;
+  const int e = p.block_expert[b];  // block_expert has num_blocks entries, -1 past the end
+  if (e < 0 || b * BM >= p.num_padded[0]) return;
+  const int s0 = grp * S;
+  const int n_str = min(S, n_strips - s0);
+
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int K = p.K, nch = (K + 127) / 128;
+  const int n_my = (nch + 3) / 4;  // chunk slots per wave and strip (the same for every wave)
+  const int TK = p.T * p.slots_per_token;
+  const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
+  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
+  const int nbn = (p.Nw + 127) / 128, nbk = nch;
+
+  // weight row of tile t in strip s for this lane (lane li = column inside the tile)
+  auto tile_col = [&](int s, int t) {
+    return (STAGE == 1) ? (s0 + s) * COLS_PER_STRIP + (t % (NT / 2)) * 16 + li
+                        : (s0 + s) * COLS_PER_STRIP + t * 16 + li;
+  };
+  auto tile_row = [&](int s, int t) {  // first weight row of the lane's tile (0 for tiles past N)
+    const int c = tile_col(s, t) - li;
+    if (c >= p.N) return 0;
+    return (STAGE == 1 && t >= NT / 2) ? p.N + c : c;
+  };
+
+  // A row of this lane in each m-tile, and the A rows of its 4 output rows
+  const uint8_t* a_src[MT];
+  bool a_ok[MT];
+  int a_idx[MT];
+  int o_idx[MT][4];
+  bool o_ok[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    int arow = b * BM + m * 16 + li;
+    bool ok = true;
+    if (STAGE == 1) {
+      const int slot = p.sorted_slots[arow];
+      ok = slot < TK;
+      arow = ok ? slot / p.slots_per_token : 0;
+    }
+    a_src[m] = (const uint8_t*)p.a + (size_t)arow * a_row_bytes;
+    a_ok[m] = ok;
+    a_idx[m] = arow;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      int orow = b * BM + m * 16 + 4 * g + rr;
+      bool ook = true;
+      if (STAGE == 1) {
+        const int slot = p.sorted_slots[orow];
+        ook = slot < TK;
+        orow = ook ? slot / p.slots_per_token : 0;
+      }
+      o_idx[m][rr] = orow;
+      o_ok[m][rr] = ook;
+    }
+  }
+
+  // Loads stream item i = (strip i / n_my, chunk slot i % n_my); past the end the
+  // last item is re-read with zero data.  Invalid elements read the zero page.
+  const int n_items = n_str * n_my;
+  auto load = [&](int i, WeightRegs<WF, NT>& wr, ARegs<AF, MT>& ar) {
+    const bool in = i < n_items;
+    const int ii = in ? i : n_items - 1;
+    const int s = ii / n_my, c = w + 4 * (ii % n_my);
+    const bool live = in && c < nch;
+    const bool kok = live && (c * 128 + 32 * g < K);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int trow = tile_row(s, t);
+      const uint8_t* wd = WLay::data(p, e, trow, li, g, lane, K);
+      if constexpr (WF == kWMxfp4) {
+        wr.w[t][0] = ld16(wd, (size_t)c * WLay::kDataStride, kok);
+        wr.s[t] = ld8(WLay::scale(p, e, trow, li, g, lane, K), (size_t)c * WLay::kScaleStride, kok);
+      } else {
+        wr.w[t][0] = ld16(wd, (size_t)c * WLay::kDataStride, kok);
+        wr.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(wd, (size_t)c * WLay::kDataStride + WLay::kHiOff, kok);
+        if constexpr (WF == kWFp8Block)
+          wr.sb[t] = ldf((const float*)p.w_scale, ((size_t)e * nbn + trow / 128) * nbk + c, live);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const bool ok = kok && a_ok[m];
+      const size_t off = (size_t)c * (NA == 4 ? 256 : (NA == 1 ? 64 : 128)) + g * (NA * 16);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) ar.a[m][q] = ld16(a_src[m], off + 16 * q, ok);
+      if constexpr (AF == kAMxfp4)
+        ar.sa[m] = ld8((const uint8_t*)p.a_scale, (size_t)a_idx[m] * (K / 32) + c * 4 + g, ok);
+      if constexpr (AF == kAFp8G128) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          ar.as[m][rr] = ldf((const float*)p.a_scale, (size_t)o_idx[m][rr] * nch + c, live && o_ok[m][rr]);
+      }
+    }
+  };
+
+  f32x4 acc[MT][NT];
+  auto clear = [&]() {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto compute = [&](const WeightRegs<WF, NT>& wr, const ARegs<AF, MT>& ar) {
+    if constexpr (AF == kABf16) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float sc = e8m0_to_f32(wr.s[t]);
+          const uint32_t dw = (uint32_t)wr.w[t][0][st];
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
+          const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ar.a[m][st]), bfr,
+                                                                 acc[m][t], 0, 0, 0);
+        }
+      }
+    } else if constexpr (AF == kAMxfp4) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const i32x8 a8 = {ar.a[m][0][0], ar.a[m][0][1], ar.a[m][0][2], ar.a[m][0][3], 0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const i32x8 b8 = {wr.w[t][0][0], wr.w[t][0][1], wr.w[t][0][2], wr.w[t][0][3], 0, 0, 0, 0};
+          acc[m][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[m][t], 4, 4, 0, (int)ar.sa[m], 0,
+                                                                        (int)wr.s[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const i32x4 lo = ar.a[m][0], hi = ar.a[m][NA - 1];
+        const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const i32x4 wl = wr.w[t][0], wh = wr.w[t][WF == kWMxfp4 ? 0 : 1];
+          const i32x8 b8 = {wl[0], wl[1], wl[2], wl[3], wh[0], wh[1], wh[2], wh[3]};
+          if constexpr (WF == kWFp8Block) {
+            const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[m][t][rr] += part[rr] * (ar.as[m][rr] * wr.sb[t]);
+          } else {
+            acc[m][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[m][t], 0, 0, 0, 127, 0, 127);
+          }
+        }
+      }
+    }
+  };
+
+  // End of strip s: partial sums of waves 1..3 go through LDS (buffer s & 1), wave 0
+  // adds them in wave order and writes the strip's outputs; accumulators restart.
+  auto finish_strip = [&](int s) {
+    const int buf = s & 1;
+    if (w > 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) red[buf][w - 1][(m * NT + t) * 4 + rr][lane] = acc[m][t][rr];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int i = (m * NT + t) * 4 + rr;
+            acc[m][t][rr] = ((acc[m][t][rr] + red[buf][0][i][lane]) + red[buf][1][i][lane]) + red[buf][2][i][lane];
+          }
+      if constexpr (STAGE == 1) {
+#pragma unroll
+        for (int t = 0; t < NT / 2; ++t) {
+          const int col = tile_col(s, t);
+          if (col >= p.N) continue;
+          const int tu = t + NT / 2;
+          const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
+          const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int row = m * 16 + 4 * g + rr;
+              float gv = acc[m][t][rr], uv = acc[m][tu][rr];
+              if constexpr (WF == kWFp8Channel) {
+                const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f;
+                gv = gv * as * wg;
+                uv = uv * as * wu;
+              }
+              const float hv = gv / (1.0f + __expf(-gv)) * uv;
+              p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(hv);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = m * 16 + 4 * g + rr;
+            const int slot = p.sorted_slots[b * BM + row];
+            if (slot >= TK) continue;
+            const float tw = p.topk_weights[slot];
+            const float as = (WF == kWFp8Channel) ? ((const float*)p.a_scale)[b * BM + row] : 1.0f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const int col = tile_col(s, t);
+              if (col >= p.N) continue;
+              float v = acc[m][t][rr];
+              if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
+              p.ybuf[(size_t)slot * p.N + col] = v * tw;
+            }
+          }
+      }
+    }
+    clear();
+  };
+
+  clear();
+  // One item in flight ahead of the MFMAs.  Each half-iteration issues the next
+  // item's loads, then computes the previous one; sched_barrier keeps the scheduler
+  // from sinking a prefetch below the MFMAs that follow it.
+  WeightRegs<WF, NT> w0, w1;
+  ARegs<AF, MT> a0, a1;
+  load(0, w0, a0);
+  for (int i = 0; i < n_items; i += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(i + 1, w1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w0, a0);
+    if ((i + 1) % n_my == 0) finish_strip(i / n_my);
+    __builtin_amdgcn_sched_barrier(0);
+    load(i + 2, w0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < n_items) {
+      compute(w1, a1);
+      if ((i + 2) % n_my == 0) finish_strip((i + 1) / n_my);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Stream kernel (16-row blocks whose activation tile fits in LDS: the decode shape).
+// The block's whole activation tile (16 rows x K, gathered token rows in stage 1) is
+// loaded into LDS once; then each of the WAVES waves streams the full K extent of its
+// own NT weight tiles from HBM straight into registers, D chunks ahead of the MFMAs,
+// reading its A operands from LDS.  Waves own disjoint output columns, so there is no
+// barrier and no cross-wave reduction after the tile load.  Compared with each wave
+// fetching its activation fragments from L2, this reads the activations once per
+// workgroup, which is what keeps a 4-bit weight stream (whose activations are four
+// times as many bytes per row) at HBM speed.
+template <int AF>
+constexpr int a_bytes_x2() { return AF == kABf16 ? 4 : (AF == kAMxfp4 ? 1 : 2); }  // 2 x bytes per element
+
+template <int STAGE, int WF, int AF, int NT, int D, int WAVES, int WL>
+__global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmParams p) {
+  using WLay = WLayout<WF, WL>;
+  constexpr int BM = 16;
+  constexpr int NTH = 64 * WAVES;
+  constexpr int COLS_PER_WAVE = (STAGE == 1) ? 8 * NT : 16 * NT;
+  constexpr int COLS_PER_WG = COLS_PER_WAVE * WAVES;
+  static_assert(STAGE == 2 || NT % 2 == 0, "stage 1 pairs gate and up tiles");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
+  const int G = p.num_blocks * n_tiles;
+  const int lid = xcd_remap((int)blockIdx.x, G);
+  const int b = lid % p.num_blocks;
+  const int nt_idx = lid / p.num_blocks;
+  const int e = p.block_expert[b];  // num_blocks entries, -1 past the end
+  if (e < 0 || b * BM >= p.num_padded[0]) return;
+
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int K = p.K, nch = (K + 127) / 128;
+  const int TK = p.T * p.slots_per_token;
+  const int row_bytes = K * a_bytes_x2<AF>() / 2;          // A bytes per row in memory
+  const int pad_bytes = nch * 128 * a_bytes_x2<AF>() / 2;   // row padded to whole chunks (zero tail)
+  const int lrow = pad_bytes + 16;                          // padded LDS row
+  const int ngp = nch * 4;                                  // MXFP4 scale bytes per LDS row (zero tail)
+  uint8_t* lds_a = smem;                                    // [16][lrow]
+  int* lds_row = (int*)(smem + BM * lrow);                  // [16] A row index, -1 = pad
+  uint8_t* lds_sc = smem + BM * lrow + 64;                  // A scales: [16][nch] f32 | [16][ngp] u8 | [16] f32
+
+  // ---- activation tile -> LDS ----
+  if (tid < BM) {
+    int arow = b * BM + tid;
+    if (STAGE == 1) {
+      const int slot = p.sorted_slots[arow];
+      arow = slot < TK ? slot / p.slots_per_token : -1;
+    }
+    lds_row[tid] = arow;
+  }
+  __syncthreads();
+  {
+    const int ppr = pad_bytes / 16;  // 16 B pieces per LDS row; those past the row's bytes are zero
+    for (int q = tid; q < BM * ppr; q += NTH) {
+      const int r = q / ppr, pc = q % ppr;
+      const int arow = lds_row[r];
+      const bool ok = arow >= 0 && 16 * pc < row_bytes;
+      const i32x4 v = ld16((const uint8_t*)p.a, (size_t)(arow < 0 ? 0 : arow) * row_bytes + 16 * pc, ok);
+      *(i32x4*)(lds_a + r * lrow + 16 * pc) = v;
+    }
+    if constexpr (AF == kAFp8G128) {
+      for (int q = tid; q < BM * nch; q += NTH) {
+        const int r = q / nch, c = q % nch, arow = lds_row[r];
+        ((float*)lds_sc)[q] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * nch + c, arow >= 0);
+      }
+    } else if constexpr (AF == kAMxfp4) {
+      const int ng = K / 32;
+      for (int q = tid; q < BM * ngp; q += NTH) {
+        const int r = q / ngp, c = q % ngp, arow = lds_row[r];
+        lds_sc[q] = (uint8_t)ld8((const uint8_t*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * ng + c, arow >= 0 && c < ng);
+      }
+    } else if constexpr (AF == kAFp8Token) {
+      if (tid < BM) {
+        const int arow = lds_row[tid];
+        ((float*)lds_sc)[tid] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- this wave's weight tiles ----
+  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
+  const int nbn = (p.Nw + 127) / 128, nbk = nch;
+  const uint8_t* w_src[NT];
+  const uint8_t* ws_src[NT];
+  const float* wsb_src[NT];
+  int col[NT];
+  bool col_ok[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int c, trow;
+    if (STAGE == 1) {
+      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + (t % (NT / 2)) * 16 + li;
+      col_ok[t] = c < p.N;
+      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
+    } else {
+      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + t * 16 + li;
+      col_ok[t] = c < p.N;
+      trow = col_ok[t] ? c - li : 0;
+    }
+    col[t] = c;
+    w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
+    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
+    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
+  }
+
+  auto load_w = [&](int c, WeightRegs<WF, NT>& r) {
+    const bool live = c < nch;
+    const int cc = live ? c : nch - 1;
+    const bool kok = live && (cc * 128 + 32 * g < K);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (WF == kWMxfp4) {
+        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
+        r.s[t] = ld8(ws_src[t], (size_t)cc * WLay::kScaleStride, kok);
+      } else {
+        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
+        r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)cc * WLay::kDataStride + WLay::kHiOff, kok);
+        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)cc, live);
+      }
+    }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int c, const WeightRegs<WF, NT>& wr) {
+    if (c >= nch) return;  // past the end: nothing to add
+    const uint8_t* arow = lds_a + li * lrow;
+    if constexpr (AF == kABf16) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 af = *(const bf16x8*)(arow + 256 * c + 64 * g + 16 * st);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float sc = e8m0_to_f32(wr.s[t]);
+          const uint32_t dw = (uint32_t)wr.w[t][0][st];
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
+          const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[t], 0, 0, 0);
+        }
+      }
+    } else if constexpr (AF == kAMxfp4) {
+      const i32x4 a4 = *(const i32x4*)(arow + 64 * c + 16 * g);
+      const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+      const int sa = (int)lds_sc[li * ngp + 4 * c + g];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const i32x8 b8 = {wr.w[t][0][0], wr.w[t][0][1], wr.w[t][0][2], wr.w[t][0][3], 0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, sa, 0, (int)wr.s[t]);
+      }
+    } else {
+      const i32x4 lo = *(const i32x4*)(arow + 128 * c + 32 * g);
+      const i32x4 hi = *(const i32x4*)(arow + 128 * c + 32 * g + 16);
+      const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float asr[4];
+      if constexpr (WF == kWFp8Block) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) asr[rr] = ((const float*)lds_sc)[(4 * g + rr) * nch + c];
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const i32x4 wl = wr.w[t][0], wh = wr.w[t][WF == kWMxfp4 ? 0 : 1];
+        const i32x8 b8 = {wl[0], wl[1], wl[2], wl[3], wh[0], wh[1], wh[2], wh[3]};
+        if constexpr (WF == kWFp8Block) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                              0, 127, 0, 127);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[t][rr] += part[rr] * (asr[rr] * wr.sb[t]);
+        } else {
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+  };
+
+  // D-deep register ring: chunk c lives in ring[c % D]; the loop is unrolled by D so
+  // every ring index is a compile-time constant.  sched_barrier keeps the prefetch of
+  // chunk c + D from being sunk below the MFMAs of chunk c.
+  WeightRegs<WF, NT> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d, ring[d]);
+  for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c0 + d, ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(c0 + d + D, ring[d]);
+    }
+  }
+
+  // ---- epilogue: this wave's columns ----
+  if constexpr (STAGE == 1) {
+#pragma unroll
+    for (int t = 0; t < NT / 2; ++t) {
+      if (!col_ok[t]) continue;
+      const int tu = t + NT / 2;
+      const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col[t]] : 1.0f;
+      const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col[t]] : 1.0f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = 4 * g + rr;
+        float gv = acc[t][rr], uv = acc[tu][rr];
+        if constexpr (WF == kWFp8Channel) {
+          const float as = ((const float*)lds_sc)[row];
+          gv = gv * as * wg;
+          uv = uv * as * wu;
+        }
+        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(hv);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 4 * g + rr;
+      const int slot = p.sorted_slots[b * BM + row];
+      if (slot >= TK) continue;
+      const float tw = p.topk_weights[slot];
+      const float as = (WF == kWFp8Channel) ? ((const float*)lds_sc)[row] : 1.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (!col_ok[t]) continue;
+        float v = acc[t][rr];
+        if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col[t]];
+        p.ybuf[(size_t)slot * p.N + col[t]] = v * tw;
+      }
+    }
+  }
+}
+
+// LDS bytes of the stream kernel's activation tile and scales.
+static size_t stream_lds_bytes(int afmt, int K) {
+  const int nch = (K + 127) / 128;
+  const size_t pad_bytes = (size_t)nch * ((afmt == kABf16) ? 256 : (afmt == kAMxfp4 ? 64 : 128));
+  size_t sc = 0;
+  if (afmt == kAFp8G128) sc = 16 * (size_t)nch * 4;
+  if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
+  if (afmt == kAFp8Token) sc = 16 * 4;
+  return 16 * (pad_bytes + 16) + 64 + sc;
+}
+
 // out[t, :] = bf16( sum_{j ascending} ybuf[t*K + j, :] ), slots with invalid ids skipped.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf, const int32_t* __restrict__ ids,
                                                       int T, int K, int H, int E, uint16_t* __restrict__ out) {
@@ -351,27 +957,80 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *(uint2*)(out + (size_t)t * H + c) = make_uint2(lo, hi);
 }
 
-template <int STAGE, int WF, int AF, int BM>
-static hipError_t launch_one(const GemmParams& p, hipStream_t stream) {
-  constexpr int NT = BM <= 32 ? 2 : 4;
-  constexpr int COLS_PER_WG = (STAGE == 1) ? 32 * NT : 64 * NT;
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 4
+#endif
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 3
+#endif
+#ifndef MOE_STREAM_WAVES
+#define MOE_STREAM_WAVES 8
+#endif
+constexpr size_t kStreamLdsMax = 100 * 1024;
+
+template <int STAGE, int WF, int AF, int WL>
+static hipError_t launch_stream(const GemmParams& p, size_t lds, hipStream_t stream) {
+  constexpr int NT = MOE_STREAM_NT, D = MOE_STREAM_DEPTH, WAVES = MOE_STREAM_WAVES;
+  constexpr int COLS_PER_WG = ((STAGE == 1) ? 8 * NT : 16 * NT) * WAVES;
   const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
   const long G = (long)p.num_blocks * n_tiles;
   if (G == 0) return hipSuccess;
   if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  moe_gemm_kernel<STAGE, WF, AF, BM, NT><<<(unsigned)G, 256, 0, stream>>>(p);
+  auto kern = moe_gemm_stream_kernel<STAGE, WF, AF, NT, D, WAVES, WL>;
+  static bool attr_set = false;  // raise the dynamic LDS limit once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)G, 64 * WAVES, lds, stream>>>(p);
   return hipGetLastError();
+}
+
+template <int STAGE, int WF, int AF, int BM, int WL>
+static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
+  if constexpr (BM == 16) {
+    const size_t lds = stream_lds_bytes(AF, p_in.K);
+    if (lds <= kStreamLdsMax) return launch_stream<STAGE, WF, AF, WL>(p_in, lds, stream);
+  }
+  constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
+  constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;
+  constexpr int COLS_PER_WG = kSplit ? ((STAGE == 1) ? 8 * NT : 16 * NT) : ((STAGE == 1) ? 32 * NT : 64 * NT);
+  GemmParams p = p_in;
+  const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
+  long groups = n_tiles;
+  if constexpr (kSplit) {
+    // strips per workgroup: about MOE_KSPLIT_WAVES_PER_CU resident workgroups' worth
+    // of (block, strip) items for each of the 256 CUs, at least one strip each
+    const long items = (long)p.num_blocks * n_tiles;
+    const long target = 256L * MOE_KSPLIT_WGS_PER_CU;
+    p.strips_per_wg = (int)std::max(1L, std::min(n_tiles, items / target));
+    groups = (n_tiles + p.strips_per_wg - 1) / p.strips_per_wg;
+  }
+  const long G = (long)p.num_blocks * groups;
+  if (G == 0) return hipSuccess;
+  if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
+  if constexpr (kSplit)
+    moe_gemm_ksplit_kernel<STAGE, WF, AF, BM, NT, WL><<<(unsigned)G, 256, 0, stream>>>(p);
+  else
+    moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL><<<(unsigned)G, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int STAGE, int WF, int AF, int WL>
+static hipError_t launch_bm_wl(int bm, const GemmParams& p, hipStream_t stream) {
+  switch (bm) {
+    case 16: return launch_one<STAGE, WF, AF, 16, WL>(p, stream);
+    case 32: return launch_one<STAGE, WF, AF, 32, WL>(p, stream);
+    case 64: return launch_one<STAGE, WF, AF, 64, WL>(p, stream);
+    case 128: return launch_one<STAGE, WF, AF, 128, WL>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int STAGE, int WF, int AF>
 static hipError_t launch_bm(int bm, const GemmParams& p, hipStream_t stream) {
-  switch (bm) {
-    case 16: return launch_one<STAGE, WF, AF, 16>(p, stream);
-    case 32: return launch_one<STAGE, WF, AF, 32>(p, stream);
-    case 64: return launch_one<STAGE, WF, AF, 64>(p, stream);
-    case 128: return launch_one<STAGE, WF, AF, 128>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return p.weight_layout ? launch_bm_wl<STAGE, WF, AF, 1>(bm, p, stream) : launch_bm_wl<STAGE, WF, AF, 0>(bm, p, stream);
 }
 
 template <int STAGE>
@@ -381,6 +1040,43 @@ static hipError_t launch_stage(int wfmt, int afmt, int bm, const GemmParams& p, 
   if (wfmt == kWFp8Block && afmt == kAFp8G128) return launch_bm<STAGE, kWFp8Block, kAFp8G128>(bm, p, stream);
   if (wfmt == kWFp8Channel && afmt == kAFp8Token) return launch_bm<STAGE, kWFp8Channel, kAFp8Token>(bm, p, stream);
   return hipErrorInvalidValue;
+}
+
+// One-time permutation into the tiled weight layout (see moe_tile_weights).  One
+// wavefront per block: lane l = 16g + r copies row r's 16 B (MXFP4) or 2 x 16 B (FP8)
+// of K elements [128c + 32g, +32) and, for MXFP4, the E8M0 byte of that 32-group.
+template <int WF>
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
+                                                           uint8_t* __restrict__ out, long n_blocks, int N, int K) {
+  const long blk = (long)blockIdx.x * 4 + threadIdx.x / 64;
+  if (blk >= n_blocks) return;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const int nch = (K + 127) / 128;
+  const int c = (int)(blk % nch);
+  const long tile = blk / nch;                       // e * (N/16) + n16
+  const long row = tile * 16 + r;                    // e * N + n
+  const bool ok = c * 128 + 32 * g < K;
+  if constexpr (WF == kWMxfp4) {
+    uint8_t* o = out + blk * 1088;
+    *(i32x4*)(o + 16 * lane) = ld16(w, row * (size_t)(K / 2) + 64 * c + 16 * g, ok);
+    o[1024 + lane] = (uint8_t)ld8(ws, row * (size_t)(K / 32) + 4 * c + g, ok);
+  } else {
+    uint8_t* o = out + blk * 2048;
+    *(i32x4*)(o + 16 * lane) = ld16(w, row * (size_t)K + 128 * c + 32 * g, ok);
+    *(i32x4*)(o + 1024 + 16 * lane) = ld16(w, row * (size_t)K + 128 * c + 32 * g + 16, ok);
+  }
+}
+
+hipError_t launch_tile_weights(int wfmt, int E, int N, int K, const uint8_t* w, const void* ws, uint8_t* out,
+                               hipStream_t stream) {
+  const long n_blocks = (long)E * (N / 16) * ((K + 127) / 128);
+  if (n_blocks == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n_blocks + 3) / 4);
+  if (wfmt == kWMxfp4)
+    tile_weights_kernel<kWMxfp4><<<grid, 256, 0, stream>>>(w, (const uint8_t*)ws, out, n_blocks, N, K);
+  else
+    tile_weights_kernel<kWFp8Block><<<grid, 256, 0, stream>>>(w, nullptr, out, n_blocks, N, K);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmParams& p, hipStream_t stream) {

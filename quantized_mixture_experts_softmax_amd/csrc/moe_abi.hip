@@ -10,6 +10,12 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_prof_on = false;
+
+hipError_t prof_mark(int i, hipStream_t stream) {
+  return g_prof_on ? hipEventRecord(g_prof[i], stream) : hipSuccess;
+}
 
 moe_status fail(moe_status st, const char* fmt, ...) {
   va_list ap;
@@ -69,6 +75,8 @@ moe_status check_shapes(const moe_forward_args* a) {
   if (!pair_supported(a->wfmt, a->afmt))
     return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)a->wfmt,
                 (int)a->afmt);
+  if (a->weight_layout != MOE_LAYOUT_CANONICAL && a->weight_layout != MOE_LAYOUT_TILED)
+    return fail(MOE_EINVAL, "unknown weight layout %d", (int)a->weight_layout);
   return ok();
 }
 
@@ -77,6 +85,35 @@ moe_status check_shapes(const moe_forward_args* a) {
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_profile_events(hipEvent_t* events, int count) {
+  if (count == 0) {
+    g_prof_on = false;
+    return ok();
+  }
+  if (count != 4 || !events) return fail(MOE_EINVAL, "moe_profile_events: pass 4 events, or count 0 to disable");
+  for (int i = 0; i < 4; ++i) g_prof[i] = events[i];
+  g_prof_on = true;
+  return ok();
+}
+
+size_t moe_tiled_weight_bytes(moe_wfmt wfmt, int E, int N, int K) {
+  if (E < 0 || N < 0 || K < 0 || N % 16 || K % 32) return 0;
+  const size_t blocks = (size_t)E * (N / 16) * ((K + 127) / 128);
+  if (wfmt == MOE_W_MXFP4) return blocks * 1088;
+  if (wfmt == MOE_W_FP8_BLOCK128 || wfmt == MOE_W_FP8_CHANNEL) return blocks * 2048;
+  return 0;
+}
+
+moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w, const void* w_scale, uint8_t* out,
+                            hipStream_t stream) {
+  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "moe_tile_weights: unknown weight format %d", (int)wfmt);
+  if (E < 0 || N <= 0 || K <= 0 || N % 16 || K % 32 || K > 65536)
+    return fail(MOE_EINVAL, "moe_tile_weights: need N %% 16 == 0, K %% 32 == 0, K <= 65536 (got N=%d, K=%d)", N, K);
+  if (E > 0 && (!w || !out || (wfmt == MOE_W_MXFP4 && !w_scale))) return fail(MOE_EINVAL, "moe_tile_weights: NULL pointer");
+  if (!aligned(w, 16) || !aligned(out, 16)) return fail(MOE_EINVAL, "moe_tile_weights: w and out must be 16-byte aligned");
+  return hip_status(moe::launch_tile_weights((int)wfmt, E, N, K, w, w_scale, out, stream), "moe_tile_weights launch");
+}
 
 moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I) {
   if (act != MOE_ACT_SILU) return fail(MOE_EUNSUPPORTED, "only the SiLU-and-mul activation is implemented");
@@ -182,8 +219,10 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   moe_status st = moe_workspace_layout(a, &L);
   if (st != MOE_OK) return st;
   if (a->T == 0) return ok();
-  if (!a->hidden_states || !a->w1 || !a->w1_scale || !a->w2 || !a->w2_scale || !a->topk_ids || !a->topk_weights ||
-      !a->sorted_slots || !a->block_expert || !a->num_padded || !a->out)
+  // tiled MXFP4 weights carry their scales inside the blocks
+  const bool scales_needed = !(a->wfmt == MOE_W_MXFP4 && a->weight_layout == MOE_LAYOUT_TILED);
+  if (!a->hidden_states || !a->w1 || !a->w2 || (scales_needed && (!a->w1_scale || !a->w2_scale)) || !a->topk_ids ||
+      !a->topk_weights || !a->sorted_slots || !a->block_expert || !a->num_padded || !a->out)
     return fail(MOE_EINVAL, "moe_experts_forward: NULL pointer");
   if (!aligned(a->hidden_states, 16) || !aligned(a->w1, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
       !aligned(a->topk_weights, 4) || !aligned(a->w1_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) ||
@@ -224,6 +263,7 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.num_padded = a->num_padded;
   p.num_blocks = (int)(cap / a->block_m);
   p.topk_weights = a->topk_weights;
+  p.weight_layout = (int)a->weight_layout;
 
   // stage 1: gate/up GEMM + SiLU-and-mul -> h (bf16, sorted rows)
   p.a = a1;
@@ -235,8 +275,10 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.K = a->H;
   p.Nw = 2 * a->I;
   p.h = h;
+  if ((e = prof_mark(0, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
   e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
+  if ((e = prof_mark(1, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
 
   // a2: re-quantise h in the activation format
   const void* a2 = h;
@@ -263,10 +305,12 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.ybuf = ybuf;
   e = moe::launch_gemm(2, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 2");
+  if ((e = prof_mark(2, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
 
   // ordered top-k combine
   e = moe::launch_combine(ybuf, a->topk_ids, a->T, a->K, a->H, a->E_total, a->out, stream);
-  return hip_status(e, "moe_experts_forward: combine");
+  if (e != hipSuccess) return hip_status(e, "moe_experts_forward: combine");
+  return hip_status(prof_mark(3, stream), "moe_experts_forward: profiling event");
 }
 
 }  // extern "C"

@@ -73,10 +73,9 @@ __device__ __forceinline__ float exp2i(int e) {
   return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
-// E8M0 byte -> fp32 scale 2^(b-127)  (255 = NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
-}
+// E8M0 byte -> fp32 scale 2^(b-127) (one v_ldexp_f32, exact down to the subnormal
+// 2^-127; the byte 255, NaN in E8M0, is not produced by any path here).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __builtin_ldexpf(1.0f, (int)b - 127); }
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {

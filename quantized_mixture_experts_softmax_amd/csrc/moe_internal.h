@@ -32,6 +32,8 @@ struct GemmParams {
   // stage 2 output: ybuf fp32 [T*K, H] by slot id, weighted by topk_weights
   float* ybuf;
   const float* topk_weights;
+  int strips_per_wg;   // small-block kernel: consecutive column strips one workgroup streams
+  int weight_layout;   // 0 canonical, 1 tiled (moe_tile_weights)
 };
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
@@ -41,6 +43,8 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, in
 // rows_dev (optional): device row count; rows at or past it are skipped.
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, const int32_t* rows_dev,
                             uint8_t* codes, void* scales, hipStream_t stream);
+hipError_t launch_tile_weights(int wfmt, int E, int N, int K, const uint8_t* w, const void* ws, uint8_t* out,
+                               hipStream_t stream);
 hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, int T, int K, int H, int E_total,
                           uint16_t* out, hipStream_t stream);

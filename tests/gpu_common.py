@@ -89,7 +89,7 @@ def check_output(got, ref: np.ndarray, what: str, max_rel=MAX_ABS_REL_RMS, row_l
     return max_rel_err, float(rows.max())
 
 
-def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dict | None = None):
+def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dict | None = None, tiled=False):
     """Route, sort, quantise and run the expert layer on the GPU through the ABI.
     Returns a dict of host copies of every intermediate."""
     wd = wd or dev_weights(data)
@@ -97,16 +97,16 @@ def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dic
     logits = to_dev(data["logits"])
     layer = B.MoELayer(wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], H=w.H, I=w.I, E=w.E, topk=w.topk,
                        wfmt=w.wfmt, afmt=w.afmt, score=score_name(w), n_shared=w.n_shared,
-                       shared_weight=w.shared_weight, block_m=block_m)
+                       shared_weight=w.shared_weight, block_m=block_m, tiled=tiled)
     out = layer(x, logits)
     torch.cuda.synchronize()
     b = layer._bufs[(x.shape[0], str(x.device))]
     res = dict(out=bf16_host(out), ids=b["ids"].cpu().numpy(), weights=b["w"].cpu().numpy(), bm=b["bm"],
                sort={k: v.cpu().numpy() for k, v in b["sort"].items()}, layer=layer, bufs=b)
     if b["workspace"] is not None:
-        args = B.forward_args(x, wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], b["ids"], b["w"], b["sort"],
+        args = B.forward_args(x, layer.w1, layer.w1_scale, layer.w2, layer.w2_scale, b["ids"], b["w"], b["sort"],
                               w.wfmt, w.afmt, b["bm"], w.E_total, w.I, b["out"], b["workspace"],
-                              *(b["a1"] if b["a1"] else (None, None)))
+                              *(b["a1"] if b["a1"] else (None, None)), weight_layout=layer.weight_layout)
         L = B.moe_workspace_layout(args)
         ws = b["workspace"]
         cap = B.moe_sort_capacity(x.shape[0], w.K, w.E_total, b["bm"])
@@ -128,3 +128,24 @@ def h_by_slot(res: dict, T: int, K: int, I: int) -> np.ndarray:
     valid = ss < T * K
     h[ss[valid]] = res["h_sorted"][:len(ss)][valid]
     return h
+
+
+def tiled_reference(wfmt: int, w: np.ndarray, ws: np.ndarray | None, K: int) -> np.ndarray:
+    """The tiled weight layout written out with numpy index arithmetic: blocks
+    [E][N/16][ceil(K/128)], lane l = 16g + r holds row r's K elements [128c + 32g, +32)."""
+    E, N = w.shape[0], w.shape[1]
+    nch = (K + 127) // 128
+    if wfmt == synth.W_MXFP4:
+        kb = K // 2
+        wp = np.zeros((E, N, nch * 64), np.uint8)
+        wp[:, :, :kb] = w
+        sp = np.zeros((E, N, nch * 4), np.uint8)
+        sp[:, :, :K // 32] = ws
+        data = wp.reshape(E, N // 16, 16, nch, 4, 16).transpose(0, 1, 3, 4, 2, 5)  # e, n16, c, g, r, byte
+        scal = sp.reshape(E, N // 16, 16, nch, 4).transpose(0, 1, 3, 4, 2)       # e, n16, c, g, r
+        out = np.concatenate([data.reshape(E, N // 16, nch, 1024), scal.reshape(E, N // 16, nch, 64)], axis=3)
+        return out.reshape(-1)
+    wp = np.zeros((E, N, nch * 128), np.uint8)
+    wp[:, :, :K] = w
+    v = wp.reshape(E, N // 16, 16, nch, 4, 2, 16).transpose(0, 1, 3, 5, 4, 2, 6)  # e, n16, c, half, g, r, byte
+    return v.reshape(-1)

@@ -110,3 +110,15 @@ def test_pick_block_m(lib):
     assert B.moe_pick_block_m(64, 4, 32) == 16
     assert B.moe_pick_block_m(8192, 4, 128) == 128
     assert B.moe_pick_block_m(256, 2, 8) == 64
+
+
+def test_tiled_weight_bytes_and_validation(lib):
+    assert lib.moe_tiled_weight_bytes(B.W_MXFP4, 32, 5760, 2880) == 32 * 360 * 23 * 1088
+    assert lib.moe_tiled_weight_bytes(B.W_FP8_BLOCK128, 2, 64, 300) == 0  # K % 32 != 0
+    assert lib.moe_tiled_weight_bytes(B.W_FP8_CHANNEL, 2, 64, 4096) == 2 * 4 * 32 * 2048
+    P = ctypes.c_void_p
+    assert lib.moe_tile_weights(B.W_MXFP4, 2, 40, 64, P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL  # N % 16
+    assert lib.moe_tile_weights(B.W_MXFP4, 2, 32, 64, P(FAKE), None, P(FAKE), None) == B.MOE_EINVAL     # no scales
+    assert lib.moe_tile_weights(7, 2, 32, 64, P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    fwd = lambda a: lib.moe_experts_forward(ctypes.byref(a), None)
+    assert fwd(_args(weight_layout=5)) == B.MOE_EINVAL

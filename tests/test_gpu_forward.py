@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from gpu_common import (B, DEV, bf16_dev, check_output, check_rounding, combine_f32, dev_weights, h_by_slot,
-                        layer_for, orc, run_layer, say, synth, to_dev)
+                        layer_for, orc, run_layer, say, synth, tiled_reference, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,11 +101,13 @@ def full_check(w, data, res, tokens=None, what=""):
 SMALL = []
 for fmt in (W4A16, W4A4, FP8B, FP8C):
     for bm in (16, 32, 64, 128):
-        SMALL.append((fmt, bm))
+        for tiled in (False, True):
+            SMALL.append((fmt, bm, tiled))
 
 
-@pytest.mark.parametrize("fmt,bm", SMALL, ids=[f"w{f[0]}a{f[1]}-bm{bm}" for f, bm in SMALL])
-def test_small_all_formats(fmt, bm):
+@pytest.mark.parametrize("fmt,bm,tiled", SMALL,
+                         ids=[f"w{f[0]}a{f[1]}-bm{bm}-{'tiled' if t else 'canon'}" for f, bm, t in SMALL])
+def test_small_all_formats(fmt, bm, tiled):
     # several K chunks with a ragged tail (H=320, I=288), ragged column strips, pad rows
     if fmt == FP8B:
         w = small(fmt, T=40, H=352, I=288, E=5, k=3, n_shared=1, score=synth.SCORE_SIGMOID)
@@ -113,10 +115,27 @@ def test_small_all_formats(fmt, bm):
         w = small(fmt, T=33, H=320, I=416, E=4, k=2)
     else:
         w = small(fmt)
-    say(f"small forward {w.name} bm={bm} T={w.T} H={w.H} I={w.I} E={w.E_total} K={w.K}")
+    say(f"small forward {w.name} bm={bm} tiled={tiled} T={w.T} H={w.H} I={w.I} E={w.E_total} K={w.K}")
     data = synth.make_all(w)
-    res = run_layer(w, data, block_m=bm)
-    full_check(w, data, res, what=f"{w.name}/bm{bm}")
+    res = run_layer(w, data, block_m=bm, tiled=tiled)
+    full_check(w, data, res, what=f"{w.name}/bm{bm}/{'tiled' if tiled else 'canon'}")
+
+
+@pytest.mark.parametrize("wfmt,N,K", [(synth.W_MXFP4, 64, 320), (synth.W_MXFP4, 576, 2880),
+                                      (synth.W_FP8_BLOCK128, 96, 352), (synth.W_FP8_CHANNEL, 32, 4096)])
+def test_tile_weights_layout(wfmt, N, K):
+    """The kernel layout is an exact permutation of the canonical codes (and scales)."""
+    rng = np.random.default_rng(N + K)
+    E = 3
+    if wfmt == synth.W_MXFP4:
+        w = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+        ws = rng.integers(100, 140, (E, N, K // 32), dtype=np.uint8)
+    else:
+        w = rng.integers(0, 256, (E, N, K), dtype=np.uint8)
+        ws = None
+    got = B.moe_tile_weights(to_dev(w), to_dev(ws) if ws is not None else None, wfmt, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), tiled_reference(wfmt, w, ws, K))
 
 
 def test_determinism_and_token_permutation():
@@ -153,13 +172,14 @@ def _sample(T, n, seed):
     return np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
 
 
-@pytest.mark.parametrize("name,n_tok", [("tiny", 64), ("decode", 64), ("prefill", 24)])
-def test_full_size_mxfp4_w4a16(name, n_tok):
+@pytest.mark.parametrize("name,n_tok,tiled", [("tiny", 64, False), ("decode", 64, False), ("decode", 64, True),
+                                              ("prefill", 24, False), ("prefill", 24, True)])
+def test_full_size_mxfp4_w4a16(name, n_tok, tiled):
     w = synth.WORKLOADS[name]
-    say(f"full-size {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.topk}")
+    say(f"full-size {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.topk} tiled={tiled}")
     data = synth.make_all(w)
-    res = run_layer(w, data)  # launch configuration of the benchmark (library-picked block_m)
-    full_check(w, data, res, tokens=_sample(w.T, n_tok, 5), what=name)
+    res = run_layer(w, data, tiled=tiled)  # library-picked block_m, as the benchmark runs it
+    full_check(w, data, res, tokens=_sample(w.T, n_tok, 5), what=f"{name}/{'tiled' if tiled else 'canon'}")
 
 
 def test_full_size_prefill_w4a4():
