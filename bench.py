@@ -232,7 +232,7 @@ def main() -> int:
     traffic = traffic_from_profiles(w.name if not args.tokens else f"{w.name}-T{w.T}")
     roof["traffic"] = traffic
     roof["kernel"] = ("stage-1 grouped GEMM (gate/up + SiLU-and-mul): "
-                      + ("moe_gemm_stream_kernel" if b["bm"] == 16 else
+                      + ("moe_gemm_persist_kernel" if b["bm"] == 16 else
                          "moe_gemm_ksplit_kernel" if b["bm"] == 32 else "moe_gemm_kernel"))
     roof["alg_bytes_per_launch"] = alg["gemm1_bytes"]
     roof["alg_flops_per_launch"] = alg["gemm1_flops"]

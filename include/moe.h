@@ -128,6 +128,19 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int K, int E_total, in
                           int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_route_align -- moe_route_topk followed by moe_align_sort (K = topk + n_shared,
+ * E_total = E + n_shared), with the same outputs bit for bit.  When E <= 64, T*K <= 4096
+ * and T*E <= 8192 both steps run in one launch of one workgroup (logits and ids stay on
+ * chip); other shapes take the two separate launches.  Arguments, layouts and limits are those of
+ * the two calls, plus E + n_shared <= 1024.  Device pointers; enqueued on `stream`.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_route_align(const float* router_logits, int T, int E, int topk, moe_score score,
+                           int renormalize, int n_shared, float shared_weight, int block_m,
+                           int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                           int32_t* expert_offsets, int32_t* sorted_slots, int32_t* block_expert,
+                           int32_t* num_padded, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_quant_act -- dynamic activation quantisation of a bf16 matrix [rows, cols].
  *
  * FP8 (e4m3fn) formats: per group (128 columns, or the whole row for MOE_A_FP8_TOKEN;

@@ -21,7 +21,7 @@ A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
 ACT_SILU = 0
 
 EXPORTED = [
-    "moe_route_topk", "moe_sort_capacity", "moe_align_sort", "moe_quant_act",
+    "moe_route_topk", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
     "moe_tiled_weight_bytes", "moe_tile_weights",
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_sort_capacity.argtypes = [I, I, I, I]
         L.moe_align_sort.restype = S
         L.moe_align_sort.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
+        L.moe_route_align.restype = S
+        L.moe_route_align.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, P, P, P]
         L.moe_quant_act.restype = S
         L.moe_quant_act.argtypes = [P, I, I, I, P, P, P]
         L.moe_experts_workspace_bytes.restype = ctypes.c_size_t
@@ -197,6 +199,35 @@ def moe_align_sort(topk_ids: torch.Tensor, E_total: int, block_m: int, out: dict
     return out
 
 
+def moe_route_align(router_logits: torch.Tensor, topk: int, block_m: int, score: str = "softmax",
+                    renormalize: bool = True, n_shared: int = 0, shared_weight: float = 1.0, topk_ids=None,
+                    topk_weights=None, out: dict | None = None, stream=None):
+    """moe_route_topk then moe_align_sort in one call (one launch for small batches);
+    returns (topk_ids, topk_weights, sort dict as moe_align_sort)."""
+    dev = _dev(router_logits)
+    assert router_logits.dtype == torch.float32 and router_logits.dim() == 2
+    T, E = router_logits.shape
+    K, E_total = topk + n_shared, E + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if out is None:
+        cap = moe_sort_capacity(T, K, E_total, block_m)
+        out = dict(
+            expert_counts=torch.empty(E_total, dtype=torch.int32, device=dev),
+            expert_offsets=torch.empty(E_total + 1, dtype=torch.int32, device=dev),
+            sorted_slots=torch.empty(cap, dtype=torch.int32, device=dev),
+            block_expert=torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+            num_padded=torch.empty(1, dtype=torch.int32, device=dev),
+        )
+    _check(lib().moe_route_align(_ptr(router_logits), T, E, topk, SCORE[score], int(renormalize), n_shared,
+                                 shared_weight, block_m, _ptr(topk_ids), _ptr(topk_weights),
+                                 _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]), _ptr(out["sorted_slots"]),
+                                 _ptr(out["block_expert"]), _ptr(out["num_padded"]), _stream(stream, dev)))
+    return topk_ids, topk_weights, out
+
+
 def quant_shapes(fmt: int, rows: int, cols: int):
     if fmt == A_MXFP4_G32:
         return (rows, cols // 2), (rows, cols // 32), torch.uint8
@@ -276,8 +307,8 @@ def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, top
 
 class MoELayer:
     """Device-resident weights of one quantised MoE expert layer and the full hot
-    path (route -> align-sort -> optional a1 quantisation -> experts forward), each
-    step one libmoe call.  Buffers are allocated on first use and reused."""
+    path: route + align-sort (one moe_route_align call), optional a1 quantisation,
+    experts forward.  Buffers are allocated on first use and reused."""
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
@@ -325,9 +356,8 @@ class MoELayer:
     def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
         T = x.shape[0]
         b = self._buffers(T, x.device)
-        moe_route_topk(router_logits, self.topk, self.score, True, self.n_shared, self.shared_weight,
-                       b["ids"], b["w"], stream)
-        moe_align_sort(b["ids"], self.E_total, b["bm"], b["sort"], stream)
+        moe_route_align(router_logits, self.topk, b["bm"], self.score, True, self.n_shared, self.shared_weight,
+                        b["ids"], b["w"], b["sort"], stream)
         a1c = a1s = None
         if self.afmt != A_BF16:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)

@@ -12,6 +12,7 @@
 // a disjoint stride of the pad sentinels and of block_expert.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -57,10 +58,36 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return wsum[w] + inc - v;
 }
 
-__global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int bm, int cap, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_padded) {
+// Rows p = start, start + stride, ... < cap: pad rows (past an expert's count inside its
+// padded run, or past the total) get the sentinel n; the first row of every block gets
+// the block's owner (-1 past the total).  offs [E + 1] and cnt [E] are the padded
+// offsets and counts.
+__device__ __forceinline__ void fill_pads_owners(const int* offs, const int* cnt, int E, int total, int n, int bm,
+                                                 int cap, int start, int stride, int32_t* __restrict__ sorted,
+                                                 int32_t* __restrict__ block_expert) {
+  for (int p = start; p < cap; p += stride) {
+    bool pad = p >= total;
+    if (!pad) {
+      int lo = 0, hi = E - 1;  // last e with offs[e] <= p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      pad = p >= offs[lo] + cnt[lo];
+      if ((p % bm) == 0) block_expert[p / bm] = lo;
+    } else if ((p % bm) == 0 && p / bm < cap / bm) {
+      block_expert[p / bm] = -1;
+    }
+    if (pad) sorted[p] = n;
+  }
+}
+
+// The sort as run by workgroup `chunk` of `nchunks` (kSortThreads threads).  `ids` may
+// point to global memory or to LDS.
+__device__ __forceinline__ void align_sort_body(const int32_t* ids, int n, int E, int bm, int cap, int chunk,
+                                                int nchunks, int32_t* __restrict__ counts_out,
+                                                int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted,
+                                                int32_t* __restrict__ block_expert, int32_t* __restrict__ num_padded) {
   __shared__ int total_cnt[kMaxExperts];
   __shared__ int before_cnt[kMaxExperts];  // becomes the running cursor
   __shared__ int offs[kMaxExperts + 1];
@@ -69,7 +96,7 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
   __shared__ int grand_total;
 
   const int tid = (int)threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int c0 = (int)blockIdx.x * kSortChunk;
+  const int c0 = chunk * kSortChunk;
   for (int e = tid; e < E; e += kSortThreads) {
     total_cnt[e] = 0;
     before_cnt[e] = 0;
@@ -91,7 +118,7 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
   if (tid == 0) offs[E] = grand_total;
   __syncthreads();
   const int total = grand_total;
-  if (blockIdx.x == 0) {
+  if (chunk == 0) {
     for (int e = tid; e < E; e += kSortThreads) {
       counts_out[e] = total_cnt[e];
       offsets_out[e] = offs[e];
@@ -129,22 +156,134 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
     __syncthreads();
   }
   // pad sentinels and block owners, a disjoint stride per workgroup
-  const int stride = (int)gridDim.x * kSortThreads;
-  for (int p = (int)blockIdx.x * kSortThreads + tid; p < cap; p += stride) {
-    bool pad = p >= total;
-    if (!pad) {
-      int lo = 0, hi = E - 1;  // last e with offs[e] <= p
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= p) lo = mid; else hi = mid - 1;
-      }
-      pad = p >= offs[lo] + total_cnt[lo];
-      if ((p % bm) == 0) block_expert[p / bm] = lo;
-    } else if ((p % bm) == 0 && p / bm < cap / bm) {
-      block_expert[p / bm] = -1;
-    }
-    if (pad) sorted[p] = n;
+  fill_pads_owners(offs, total_cnt, E, total, n, bm, cap, chunk * kSortThreads + tid, nchunks * kSortThreads, sorted,
+                   block_expert);
+}
+
+__global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int bm, int cap, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  align_sort_body(ids, n, E, bm, cap, (int)blockIdx.x, (int)gridDim.x, counts_out, offsets_out, sorted, block_expert,
+                  num_padded);
+}
+
+// Router + sort in one workgroup (route_sort_fusable: E <= 64, small batch).  The
+// logits are staged in LDS (row stride E + 1, so the lanes of a wave, which hold
+// different tokens, hit different banks).  Waves take (expert e, group of 64 tokens)
+// tasks: lane t counts the experts ranking before e in its token (an expert j < e
+// ranks before on >=, j > e on >, the id tie rule), the lanes of rank < k are the
+// token's winners, and the wave's ballot of them is the 64-token selection mask of e.
+// Because an expert is chosen at most once per token, the stable position of slot
+// (t, j) inside expert e is the number of earlier tokens choosing e: the masks' popcount
+// prefix over token groups plus the popcount of the lower lanes.  Shared experts are
+// chosen by every token, at position t.  Ids, weights and the sort equal those of the
+// separate router and align-sort kernels.
+constexpr int kFuseLogits = 8192;  // T * E limit of the fused kernel
+constexpr int kFuseMasks = 192;    // >= E * ceil(T / 64) when T * E <= kFuseLogits, E <= 64
+
+__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
+    const float* __restrict__ logits, int T, int E, int topk, int score, int renorm, int n_shared, float shared_w,
+    int bm, int cap, int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ float lg[kFuseLogits + kSortChunk];  // [T][E + 1]; T <= kSortChunk
+  __shared__ float sel_v[kSortChunk];             // [T][topk] winning logits by rank
+  __shared__ int sel_e[kSortChunk];               // [T][topk] winning experts by rank
+  __shared__ unsigned long long mask[kFuseMasks]; // [E][G] selection masks
+  __shared__ int pre[kFuseMasks];                 // [E][G] selections in earlier groups
+  __shared__ int cnt[kSmallE + 32];
+  __shared__ int offs[kSmallE + 32 + 1];
+  __shared__ int wsum[kSortWaves];
+  __shared__ int grand_total;
+  const int tid = (int)threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int KP = topk + n_shared, Et = E + n_shared, n = T * KP, G = (T + kWave - 1) / kWave, ld = E + 1;
+
+  for (int i = tid; i < T * E; i += kSortThreads) {
+    const int t = i / E;
+    lg[t * ld + (i - t * E)] = logits[i];
   }
+  __syncthreads();
+  for (int task = w; task < E * G; task += kSortWaves) {  // wave-uniform
+    const int e = task / G, g = task - e * G, t = g * kWave + lane;
+    const bool ok = t < T;
+    const float* row = lg + (ok ? t : 0) * ld;
+    const float v = row[e];
+    int rank = 0;
+    for (int j = 0; j < e; ++j) rank += row[j] >= v ? 1 : 0;
+    for (int j = e + 1; j < E; ++j) rank += row[j] > v ? 1 : 0;
+    const bool sel = ok && rank < topk;
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0) mask[task] = m;
+    if (sel) {
+      sel_e[t * topk + rank] = e;
+      sel_v[t * topk + rank] = v;
+    }
+  }
+  __syncthreads();
+  // per-expert counts (shared experts: every token) and group prefixes
+  if (tid < Et) {
+    int c = T;
+    if (tid < E) {
+      c = 0;
+      for (int g = 0; g < G; ++g) {
+        pre[tid * G + g] = c;
+        c += __popcll(mask[tid * G + g]);
+      }
+    }
+    cnt[tid] = c;
+  }
+  __syncthreads();
+  const int padded = tid < Et ? (cnt[tid] + bm - 1) / bm * bm : 0;
+  const int off = block_exclusive_scan(padded, wsum, &grand_total);
+  if (tid < Et) offs[tid] = off;
+  if (tid == 0) offs[Et] = grand_total;
+  __syncthreads();
+  const int total = grand_total;
+  if (tid < Et) {
+    counts_out[tid] = cnt[tid];
+    offsets_out[tid] = offs[tid];
+  }
+  if (tid == 0) {
+    offsets_out[Et] = total;
+    num_padded[0] = total;
+  }
+  // slots: ids, weights and their sorted rows
+  for (int q = tid; q < n; q += kSortThreads) {
+    const int t = q / KP, j = q - t * KP;
+    int e, pos;
+    float wt;
+    if (j < topk) {
+      e = sel_e[t * topk + j];
+      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, lg + t * ld, E);
+      const int g = t / kWave, l = t % kWave;
+      const unsigned long long below = l ? (~0ull >> (kWave - l)) : 0ull;
+      pos = offs[e] + pre[e * G + g] + __popcll(mask[e * G + g] & below);
+    } else {
+      e = E + (j - topk);
+      wt = shared_w;
+      pos = offs[e] + t;
+    }
+    ids[q] = e;
+    weights[q] = wt;
+    sorted[pos] = q;
+  }
+  fill_pads_owners(offs, cnt, Et, total, n, bm, cap, tid, kSortThreads, sorted, block_expert);
+}
+
+bool route_sort_fusable(int T, int E, int K) {
+  return E <= kSmallE && (long)T * K <= kSortChunk && (long)T * E <= kFuseLogits;
+}
+
+hipError_t launch_route_sort(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
+                             float shared_w, int bm, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream) {
+  const int K = topk + n_shared, E_total = E + n_shared;
+  if (!route_sort_fusable(T, E, K)) return hipErrorInvalidValue;
+  const int cap = T * K + E_total * (bm - 1);
+  route_sort_kernel<<<1, kSortThreads, 0, stream>>>(logits, T, E, topk, score, renorm, n_shared, shared_w, bm, cap, ids,
+                                                    weights, counts, offsets, sorted, block_expert, num_padded);
+  return hipGetLastError();
 }
 
 hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, int32_t* counts, int32_t* offsets,

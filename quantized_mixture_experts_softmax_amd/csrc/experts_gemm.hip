@@ -703,13 +703,26 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
 template <int AF>
 constexpr int a_bytes_x2() { return AF == kABf16 ? 4 : (AF == kAMxfp4 ? 1 : 2); }  // 2 x bytes per element
 
-template <int STAGE, int WF, int AF, int NT, int D, int WAVES, int WL>
+// LDS bytes of the stream kernel's activation tile, row table and scales, rounded to 16.
+__host__ __device__ inline size_t stream_lds_tile_bytes(int afmt, int K) {
+  const int nch = (K + 127) / 128;
+  const size_t pad_bytes = (size_t)nch * ((afmt == kABf16) ? 256 : (afmt == kAMxfp4 ? 64 : 128));
+  size_t sc = 0;
+  if (afmt == kAFp8G128) sc = 16 * (size_t)nch * 4;
+  if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
+  if (afmt == kAFp8Token) sc = 16 * 4;
+  return (16 * (pad_bytes + 16) + 64 + sc + 15) / 16 * 16;
+}
+
+template <int STAGE, int WF, int AF, int NT, int D, int WAVES, int KS, int WL>
 __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int BM = 16;
   constexpr int NTH = 64 * WAVES;
+  constexpr int NG = WAVES / KS;  // column groups; KS waves (contiguous K ranges) per group
+  static_assert(WAVES % KS == 0, "waves split evenly over K");
   constexpr int COLS_PER_WAVE = (STAGE == 1) ? 8 * NT : 16 * NT;
-  constexpr int COLS_PER_WG = COLS_PER_WAVE * WAVES;
+  constexpr int COLS_PER_WG = COLS_PER_WAVE * NG;
   static_assert(STAGE == 2 || NT % 2 == 0, "stage 1 pairs gate and up tiles");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -721,8 +734,12 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
   const int e = p.block_expert[b];  // num_blocks entries, -1 past the end
   if (e < 0 || b * BM >= p.num_padded[0]) return;
 
-  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int wv = tid >> 6, w = wv % NG, kp = wv / NG;  // column group, K part
   const int K = p.K, nch = (K + 127) / 128;
+  const int cpk = (nch + KS - 1) / KS;                 // chunk slots per K part
+  const int c_begin = kp * cpk;
+  const int n_loc = max(0, min(nch, c_begin + cpk) - c_begin);
   const int TK = p.T * p.slots_per_token;
   const int row_bytes = K * a_bytes_x2<AF>() / 2;          // A bytes per row in memory
   const int pad_bytes = nch * 128 * a_bytes_x2<AF>() / 2;   // row padded to whole chunks (zero tail)
@@ -731,6 +748,56 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
   uint8_t* lds_a = smem;                                    // [16][lrow]
   int* lds_row = (int*)(smem + BM * lrow);                  // [16] A row index, -1 = pad
   uint8_t* lds_sc = smem + BM * lrow + 64;                  // A scales: [16][nch] f32 | [16][ngp] u8 | [16] f32
+
+  // ---- this wave's weight tiles ----
+  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
+  const int nbn = (p.Nw + 127) / 128, nbk = nch;
+  const uint8_t* w_src[NT];
+  const uint8_t* ws_src[NT];
+  const float* wsb_src[NT];
+  int col[NT];
+  bool col_ok[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int c, trow;
+    if (STAGE == 1) {
+      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + (t % (NT / 2)) * 16 + li;
+      col_ok[t] = c < p.N;
+      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
+    } else {
+      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + t * 16 + li;
+      col_ok[t] = c < p.N;
+      trow = col_ok[t] ? c - li : 0;
+    }
+    col[t] = c;
+    w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
+    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
+    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
+  }
+
+  // j = chunk slot of this wave's K part; slots past its range read the zero page
+  auto load_w = [&](int j, WeightRegs<WF, NT>& r) {
+    const bool live = j < n_loc;
+    const int cc = min(nch - 1, c_begin + (live ? j : max(n_loc - 1, 0)));
+    const bool kok = live && (cc * 128 + 32 * g < K);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (WF == kWMxfp4) {
+        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
+        r.s[t] = ld8(ws_src[t], (size_t)cc * WLay::kScaleStride, kok);
+      } else {
+        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
+        r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)cc * WLay::kDataStride + WLay::kHiOff, kok);
+        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)cc, live);
+      }
+    }
+  };
+
+  // The first D weight chunks do not depend on the activation tile: start streaming
+  // them before the tile is loaded so HBM is busy from the first cycle.
+  WeightRegs<WF, NT> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d, ring[d]);
 
   // ---- activation tile -> LDS ----
   if (tid < BM) {
@@ -771,55 +838,15 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
   }
   __syncthreads();
 
-  // ---- this wave's weight tiles ----
-  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
-  const int nbn = (p.Nw + 127) / 128, nbk = nch;
-  const uint8_t* w_src[NT];
-  const uint8_t* ws_src[NT];
-  const float* wsb_src[NT];
-  int col[NT];
-  bool col_ok[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int c, trow;
-    if (STAGE == 1) {
-      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + (t % (NT / 2)) * 16 + li;
-      col_ok[t] = c < p.N;
-      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
-    } else {
-      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + t * 16 + li;
-      col_ok[t] = c < p.N;
-      trow = col_ok[t] ? c - li : 0;
-    }
-    col[t] = c;
-    w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
-    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
-    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
-  }
-
-  auto load_w = [&](int c, WeightRegs<WF, NT>& r) {
-    const bool live = c < nch;
-    const int cc = live ? c : nch - 1;
-    const bool kok = live && (cc * 128 + 32 * g < K);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if constexpr (WF == kWMxfp4) {
-        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
-        r.s[t] = ld8(ws_src[t], (size_t)cc * WLay::kScaleStride, kok);
-      } else {
-        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
-        r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)cc * WLay::kDataStride + WLay::kHiOff, kok);
-        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)cc, live);
-      }
-    }
-  };
-
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int c, const WeightRegs<WF, NT>& wr) {
-    if (c >= nch) return;  // past the end: nothing to add
+  auto compute = [&](int j, const WeightRegs<WF, NT>& wr) {
+    // Past the wave's range the weights are zero (zero-page loads); reading a valid
+    // activation chunk keeps the operands finite, so those MFMAs add exactly zero and the
+    // loop stays branch-free.
+    const int c = min(nch - 1, c_begin + min(j, max(n_loc - 1, 0)));
     const uint8_t* arow = lds_a + li * lrow;
     if constexpr (AF == kABf16) {
 #pragma unroll
@@ -874,10 +901,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
   // D-deep register ring: chunk c lives in ring[c % D]; the loop is unrolled by D so
   // every ring index is a compile-time constant.  sched_barrier keeps the prefetch of
   // chunk c + D from being sunk below the MFMAs of chunk c.
-  WeightRegs<WF, NT> ring[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_w(d, ring[d]);
-  for (int c0 = 0; c0 < nch; c0 += D) {
+  for (int c0 = 0; c0 < cpk; c0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       __builtin_amdgcn_sched_barrier(0);
@@ -885,6 +909,26 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
       __builtin_amdgcn_sched_barrier(0);
       load_w(c0 + d + D, ring[d]);
     }
+  }
+
+  // K parts 1..KS-1 hand their partial sums to part 0 through LDS; part 0 adds them in
+  // part order (deterministic) and runs the epilogue.
+  if constexpr (KS > 1) {
+    float* red = (float*)(smem + stream_lds_tile_bytes(AF, K));  // [KS-1][NG][NT*4][64]
+    if (kp > 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) red[(((kp - 1) * NG + w) * NT * 4 + t * 4 + rr) * 64 + lane] = acc[t][rr];
+    }
+    __syncthreads();
+    if (kp > 0) return;
+#pragma unroll
+    for (int q = 1; q < KS; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[t][rr] += red[(((q - 1) * NG + w) * NT * 4 + t * 4 + rr) * 64 + lane];
   }
 
   // ---- epilogue: this wave's columns ----
@@ -927,15 +971,290 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmP
   }
 }
 
-// LDS bytes of the stream kernel's activation tile and scales.
-static size_t stream_lds_bytes(int afmt, int K) {
-  const int nch = (K + 127) / 128;
-  const size_t pad_bytes = (size_t)nch * ((afmt == kABf16) ? 256 : (afmt == kAMxfp4 ? 64 : 128));
-  size_t sc = 0;
-  if (afmt == kAFp8G128) sc = 16 * (size_t)nch * 4;
-  if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
-  if (afmt == kAFp8Token) sc = 16 * 4;
-  return 16 * (pad_bytes + 16) + 64 + sc;
+// ---------------------------------------------------------------------------------
+// Persistent 16-row kernel (the decode shape, activation tile in LDS).  The grid is
+// one resident workgroup per slot of the chip.  The work of a launch is the list of
+// (block, column unit) pairs, a unit being two 16-column weight tiles (gate and up of
+// 16 output columns in stage 1, 32 adjacent output columns in stage 2), and each
+// workgroup takes an equal contiguous range of that list.  Inside the range, one phase
+// per block: the block's activation tile is staged in LDS once, and the phase's
+// (unit, 128-K chunk) steps are split into equal contiguous runs, one per wave.  A wave
+// streams its run through a D-deep register ring without a break at unit boundaries
+// and writes each unit it covers whole; a unit shared by consecutive waves is summed
+// by the wave that holds its first chunk, adding the later waves' partials from LDS in
+// wave order (a fixed order, so results do not depend on timing).  Compared with one
+// workgroup per column strip, the HBM stream of a CU never drains between strips, and
+// the load is balanced to within one unit per workgroup.
+template <int STAGE, int WF, int AF, int D, int WAVES, int WL>
+__global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const GemmParams p) {
+  using WLay = WLayout<WF, WL>;
+  constexpr int BM = 16, NT = 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps run bookkeeping scalar
+  const int K = p.K, nch = (K + 127) / 128;
+  const int U = (STAGE == 1) ? (p.N + 15) / 16 : (p.N + 31) / 32;  // units per block
+  const int nb = min(p.num_padded[0] / BM, p.num_blocks);          // blocks in use
+  const long L = (long)nb * U;
+  const int P = (int)gridDim.x;
+  const int wg = xcd_remap((int)blockIdx.x, P);  // neighbouring ranges (same block) share an XCD
+  long u_next = L * wg / P;
+  const long r_end = L * (wg + 1) / P;
+
+  const int TK = p.T * p.slots_per_token;
+  const int row_bytes = K * a_bytes_x2<AF>() / 2;
+  const int pad_bytes = nch * 128 * a_bytes_x2<AF>() / 2;
+  const int lrow = pad_bytes + 16;
+  const int ngp = nch * 4;
+  uint8_t* lds_a = smem;
+  int* lds_row = (int*)(smem + BM * lrow);
+  uint8_t* lds_sc = smem + BM * lrow + 64;
+  float* lds_part = (float*)(smem + stream_lds_tile_bytes(AF, K));  // [WAVES][NT*4][64]
+
+  const size_t nbn = (size_t)(p.Nw + 127) / 128;
+
+  while (u_next < r_end) {
+    const int b = (int)(u_next / U);
+    const int ua = (int)(u_next - (long)b * U);
+    const int ub = (int)min((long)U, r_end - (long)b * U);
+    u_next = (long)b * U + ub;
+    const int e = p.block_expert[b];
+    if (e < 0) continue;  // workgroup-uniform
+
+    const int S = (ub - ua) * nch;  // steps of the phase
+    const int s0 = (int)((long)S * wv / WAVES), s1 = (int)((long)S * (wv + 1) / WAVES);
+    const int n = s1 - s0;          // this wave's steps (may be 0)
+
+    // weight tile t of unit u (relative to ua): first weight row, and whether it exists
+    auto trow_of = [&](int u, int t) { return STAGE == 1 ? (t == 0 ? 16 * (ua + u) : p.N + 16 * (ua + u)) : 32 * (ua + u) + 16 * t; };
+    auto tok_of = [&](int u, int t) { return STAGE == 1 ? true : 32 * (ua + u) + 16 * t < p.N; };
+
+    // load cursor (unit, chunk) of the next step to fetch
+    int lu = s0 / nch, lc = s0 % nch, lj = 0;
+    auto load_next = [&](WeightRegs<WF, NT>& r) {
+      const bool live = lj < n;
+      const bool kok = live && (lc * 128 + 32 * g < K);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bool tok = live && tok_of(lu, t);
+        const bool ok = kok && tok;
+        const int trow = tok ? trow_of(lu, t) : 0;  // the K-tail check is per lane; the block scale is not
+        const uint8_t* src = WLay::data(p, e, trow, li, g, lane, K);
+        r.w[t][0] = ld16(src, (size_t)lc * WLay::kDataStride, ok);
+        if constexpr (WF == kWMxfp4) {
+          r.s[t] = ld8(WLay::scale(p, e, trow, li, g, lane, K), (size_t)lc * WLay::kScaleStride, ok);
+        } else {
+          r.w[t][1] = ld16(src, (size_t)lc * WLay::kDataStride + WLay::kHiOff, ok);
+          if constexpr (WF == kWFp8Block)
+            r.sb[t] = ldf((const float*)p.w_scale, ((size_t)e * nbn + trow / 128) * nch + lc, tok);
+        }
+      }
+      if (live) {
+        ++lj;
+        if (++lc == nch) { lc = 0; ++lu; }
+      }
+    };
+
+    __syncthreads();  // the previous phase is done with LDS
+    WeightRegs<WF, NT> ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_next(ring[d]);
+
+    // ---- activation tile -> LDS ----
+    if (tid < BM) {
+      int arow = b * BM + tid;
+      if (STAGE == 1) {
+        const int slot = p.sorted_slots[arow];
+        arow = slot < TK ? slot / p.slots_per_token : -1;
+      }
+      lds_row[tid] = arow;
+    }
+    __syncthreads();
+    {
+      const int ppr = pad_bytes / 16;
+      for (int q = tid; q < BM * ppr; q += 64 * WAVES) {
+        const int r = q / ppr, pc = q % ppr;
+        const int arow = lds_row[r];
+        const bool ok = arow >= 0 && 16 * pc < row_bytes;
+        const i32x4 v = ld16((const uint8_t*)p.a, (size_t)(arow < 0 ? 0 : arow) * row_bytes + 16 * pc, ok);
+        *(i32x4*)(lds_a + r * lrow + 16 * pc) = v;
+      }
+      if constexpr (AF == kAFp8G128) {
+        for (int q = tid; q < BM * nch; q += 64 * WAVES) {
+          const int r = q / nch, c = q % nch, arow = lds_row[r];
+          ((float*)lds_sc)[q] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * nch + c, arow >= 0);
+        }
+      } else if constexpr (AF == kAMxfp4) {
+        const int ng = K / 32;
+        for (int q = tid; q < BM * ngp; q += 64 * WAVES) {
+          const int r = q / ngp, c = q % ngp, arow = lds_row[r];
+          lds_sc[q] = (uint8_t)ld8((const uint8_t*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * ng + c, arow >= 0 && c < ng);
+        }
+      } else if constexpr (AF == kAFp8Token) {
+        if (tid < BM) {
+          const int arow = lds_row[tid];
+          ((float*)lds_sc)[tid] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
+        }
+      }
+    }
+    __syncthreads();
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c, const WeightRegs<WF, NT>& wr) {
+      const uint8_t* arow = lds_a + li * lrow;
+      if constexpr (AF == kABf16) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8 af = *(const bf16x8*)(arow + 256 * c + 64 * g + 16 * st);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const float sc = e8m0_to_f32(wr.s[t]);
+            const uint32_t dw = (uint32_t)wr.w[t][0][st];
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
+            const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[t], 0, 0, 0);
+          }
+        }
+      } else if constexpr (AF == kAMxfp4) {
+        const i32x4 a4 = *(const i32x4*)(arow + 64 * c + 16 * g);
+        const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+        const int sa = (int)lds_sc[li * ngp + 4 * c + g];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const i32x8 b8 = {wr.w[t][0][0], wr.w[t][0][1], wr.w[t][0][2], wr.w[t][0][3], 0, 0, 0, 0};
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, sa, 0, (int)wr.s[t]);
+        }
+      } else {
+        const i32x4 lo = *(const i32x4*)(arow + 128 * c + 32 * g);
+        const i32x4 hi = *(const i32x4*)(arow + 128 * c + 32 * g + 16);
+        const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        float asr[4];
+        if constexpr (WF == kWFp8Block) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) asr[rr] = ((const float*)lds_sc)[(4 * g + rr) * nch + c];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const i32x4 wl = wr.w[t][0], wh = wr.w[t][WF == kWMxfp4 ? 0 : 1];
+          const i32x8 b8 = {wl[0], wl[1], wl[2], wl[3], wh[0], wh[1], wh[2], wh[3]};
+          if constexpr (WF == kWFp8Block) {
+            const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                                0, 0, 127, 0, 127);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[t][rr] += part[rr] * (asr[rr] * wr.sb[t]);
+          } else {
+            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 0, 0, 0, 127, 0, 127);
+          }
+        }
+      }
+    };
+
+    // Writes unit u's outputs from a complete sum.
+    auto emit = [&](int u) {
+      if constexpr (STAGE == 1) {
+        const int col = 16 * (ua + u) + li;
+        const float wg_s = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
+        const float wu_s = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = 4 * g + rr;
+          float gv = acc[0][rr], uv = acc[1][rr];
+          if constexpr (WF == kWFp8Channel) {
+            const float as = ((const float*)lds_sc)[row];
+            gv = gv * as * wg_s;
+            uv = uv * as * wu_s;
+          }
+          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = 4 * g + rr;
+          const int slot = p.sorted_slots[b * BM + row];
+          if (slot >= TK) continue;
+          const float tw = p.topk_weights[slot];
+          const float as = (WF == kWFp8Channel) ? ((const float*)lds_sc)[row] : 1.0f;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int col = 32 * (ua + u) + 16 * t + li;
+            if (col >= p.N) continue;
+            float v = acc[t][rr];
+            if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
+            p.ybuf[(size_t)slot * p.N + col] = v * tw;
+          }
+        }
+      }
+    };
+
+    // compute cursor; a run that starts inside a unit hands that unit's sum to LDS,
+    // a run that ends inside a unit it started keeps the sum for the reduction below
+    int cu = s0 / nch, cc = s0 % nch;
+    const int head_unit = (s0 % nch != 0) ? cu : -1;
+    bool tail_open = false;
+    for (int j0 = 0; j0 < n; j0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int j = j0 + d;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cc, ring[d]);  // past the run the weights are zero: adds exact zeros
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(ring[d]);
+        if (j < n) {
+          const bool unit_end = cc == nch - 1;
+          if (unit_end || j == n - 1) {
+            if (cu == head_unit) {
+              float* dst = lds_part + (size_t)wv * NT * 4 * 64;
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) dst[(t * 4 + rr) * 64 + lane] = acc[t][rr];
+            } else if (unit_end) {
+              emit(cu);
+            } else {
+              tail_open = true;
+            }
+            if (!tail_open) {
+#pragma unroll
+              for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+          if (j + 1 < n) {
+            if (++cc == nch) { cc = 0; ++cu; }
+          }
+        }
+      }
+    }
+    __syncthreads();  // partials of shared units are in LDS
+    if (tail_open) {
+      const int u_end = (cu + 1) * nch;  // first step past the open unit
+      for (int q = wv + 1; q < WAVES; ++q) {
+        const int q0 = (int)((long)S * q / WAVES), q1 = (int)((long)S * (q + 1) / WAVES);
+        if (q0 >= u_end) break;
+        if (q1 > q0) {
+          const float* src = lds_part + (size_t)q * NT * 4 * 64;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[t][rr] += src[(t * 4 + rr) * 64 + lane];
+        }
+      }
+      emit(cu);
+    }
+  }
+}
+
+// LDS bytes of the stream kernel: activation tile, row table and scales (16 B aligned),
+// then the cross-part reduction area.
+static size_t stream_lds_bytes(int afmt, int K, int ks, int ng, int nt) {
+  return stream_lds_tile_bytes(afmt, K) + (size_t)(ks - 1) * ng * nt * 4 * 64 * 4;
 }
 
 // out[t, :] = bf16( sum_{j ascending} ybuf[t*K + j, :] ), slots with invalid ids skipped.
@@ -966,17 +1285,75 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #ifndef MOE_STREAM_WAVES
 #define MOE_STREAM_WAVES 8
 #endif
-constexpr size_t kStreamLdsMax = 100 * 1024;
+#ifndef MOE_STREAM_KSPLIT
+#define MOE_STREAM_KSPLIT 1
+#endif
+constexpr size_t kStreamLdsMax = 128 * 1024;
+#ifndef MOE_BM16_PERSIST
+#define MOE_BM16_PERSIST 1
+#endif
+#ifndef MOE_PERSIST_WAVES
+#define MOE_PERSIST_WAVES 16
+#endif
+#ifndef MOE_PERSIST_DEPTH_F4
+#define MOE_PERSIST_DEPTH_F4 6
+#endif
+#ifndef MOE_PERSIST_DEPTH_F8
+#define MOE_PERSIST_DEPTH_F8 3
+#endif
+#ifndef MOE_PERSIST_DEPTH_F8B
+#define MOE_PERSIST_DEPTH_F8B 2
+#endif
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// LDS bytes of the persistent kernel: activation tile + one partial-sum slot per wave.
+static size_t persist_lds_bytes(int afmt, int K, int waves) {
+  return stream_lds_tile_bytes(afmt, K) + (size_t)waves * 2 * 4 * 64 * 4;
+}
+
+template <int STAGE, int WF, int AF, int WL>
+static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t stream) {
+  constexpr int WAVES = MOE_PERSIST_WAVES;
+  constexpr int D = (WF == kWMxfp4) ? MOE_PERSIST_DEPTH_F4 : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
+  if (p.num_blocks == 0) return hipSuccess;
+  auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 64 * WAVES, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  // no more workgroups than units of work: (blocks x units) bounds what can be split
+  const long units = (long)p.num_blocks * ((STAGE == 1) ? (p.N + 15) / 16 : (p.N + 31) / 32);
+  const long grid = std::max(1L, std::min((long)device_cus() * per_cu, units));
+  kern<<<(unsigned)grid, 64 * WAVES, lds, stream>>>(p);
+  return hipGetLastError();
+}
 
 template <int STAGE, int WF, int AF, int WL>
 static hipError_t launch_stream(const GemmParams& p, size_t lds, hipStream_t stream) {
-  constexpr int NT = MOE_STREAM_NT, D = MOE_STREAM_DEPTH, WAVES = MOE_STREAM_WAVES;
-  constexpr int COLS_PER_WG = ((STAGE == 1) ? 8 * NT : 16 * NT) * WAVES;
+  constexpr int NT = MOE_STREAM_NT, D = MOE_STREAM_DEPTH, WAVES = MOE_STREAM_WAVES, KS = MOE_STREAM_KSPLIT;
+  constexpr int COLS_PER_WG = ((STAGE == 1) ? 8 * NT : 16 * NT) * (WAVES / KS);
   const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
   const long G = (long)p.num_blocks * n_tiles;
   if (G == 0) return hipSuccess;
   if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  auto kern = moe_gemm_stream_kernel<STAGE, WF, AF, NT, D, WAVES, WL>;
+  auto kern = moe_gemm_stream_kernel<STAGE, WF, AF, NT, D, WAVES, KS, WL>;
   static bool attr_set = false;  // raise the dynamic LDS limit once per process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
@@ -990,8 +1367,14 @@ static hipError_t launch_stream(const GemmParams& p, size_t lds, hipStream_t str
 template <int STAGE, int WF, int AF, int BM, int WL>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
-    const size_t lds = stream_lds_bytes(AF, p_in.K);
-    if (lds <= kStreamLdsMax) return launch_stream<STAGE, WF, AF, WL>(p_in, lds, stream);
+    if (MOE_BM16_PERSIST) {
+      const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
+      if (lds <= kStreamLdsMax) return launch_persist<STAGE, WF, AF, WL>(p_in, lds, stream);
+    } else {
+      const size_t lds = stream_lds_bytes(AF, p_in.K, MOE_STREAM_KSPLIT, MOE_STREAM_WAVES / MOE_STREAM_KSPLIT,
+                                          MOE_STREAM_NT);
+      if (lds <= kStreamLdsMax) return launch_stream<STAGE, WF, AF, WL>(p_in, lds, stream);
+    }
   }
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;

@@ -171,6 +171,38 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int K, int E_total, in
                     "moe_align_sort launch");
 }
 
+moe_status moe_route_align(const float* router_logits, int T, int E, int topk, moe_score score, int renormalize,
+                           int n_shared, float shared_weight, int block_m, int32_t* topk_ids, float* topk_weights,
+                           int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
+                           int32_t* block_expert, int32_t* num_padded, hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_route_align: T must be >= 0 (got %d)", T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "moe_route_align: E must be in [1, 1024] (got %d)", E);
+  if (topk < 1 || topk > E || topk > 32) return fail(MOE_EINVAL, "moe_route_align: topk must be in [1, min(E, 32)] (got %d)", topk);
+  if (n_shared < 0 || n_shared > 32) return fail(MOE_EINVAL, "moe_route_align: n_shared must be in [0, 32] (got %d)", n_shared);
+  if (E + n_shared > 1024) return fail(MOE_EINVAL, "moe_route_align: E + n_shared must be <= 1024 (got %d)", E + n_shared);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return fail(MOE_EINVAL, "moe_route_align: unknown score %d", (int)score);
+  if (!valid_bm(block_m)) return fail(MOE_EINVAL, "moe_route_align: block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+  const int K = topk + n_shared, E_total = E + n_shared;
+  if ((long long)T * K + (long long)E_total * block_m >= 0x7FFFFFFFLL) return fail(MOE_EINVAL, "moe_route_align: T*K too large");
+  if (!expert_counts || !expert_offsets || !sorted_slots || !block_expert || !num_padded ||
+      (T > 0 && (!router_logits || !topk_ids || !topk_weights)))
+    return fail(MOE_EINVAL, "moe_route_align: NULL pointer");
+  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "moe_route_align: pointers must be 4-byte aligned");
+  if (moe::route_sort_fusable(T, E, K))
+    return hip_status(moe::launch_route_sort(router_logits, T, E, topk, (int)score, renormalize ? 1 : 0, n_shared,
+                                             shared_weight, block_m, topk_ids, topk_weights, expert_counts,
+                                             expert_offsets, sorted_slots, block_expert, num_padded, stream),
+                      "moe_route_align launch");
+  moe_status st = hip_status(moe::launch_route_topk(router_logits, T, E, topk, (int)score, renormalize ? 1 : 0,
+                                                    n_shared, shared_weight, topk_ids, topk_weights, stream),
+                             "moe_route_align route launch");
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_align_sort(topk_ids, T, K, E_total, block_m, expert_counts, expert_offsets,
+                                           sorted_slots, block_expert, num_padded, stream),
+                    "moe_route_align sort launch");
+}
+
 moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt, uint8_t* codes, void* scales,
                          hipStream_t stream) {
   if (fmt != MOE_A_MXFP4_G32 && fmt != MOE_A_FP8_G128 && fmt != MOE_A_FP8_TOKEN)

@@ -40,6 +40,12 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int sc
                              float shared_w, int32_t* ids, float* weights, hipStream_t stream);
 hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, int32_t* counts, int32_t* offsets,
                              int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
+// Router + align-sort in a single one-workgroup launch; only when route_sort_fusable(T, E, K)
+// (E routed experts, K = topk + n_shared), else hipErrorInvalidValue.
+bool route_sort_fusable(int T, int E, int K);
+hipError_t launch_route_sort(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
+                             float shared_w, int bm, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 // rows_dev (optional): device row count; rows at or past it are skipped.
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, const int32_t* rows_dev,
                             uint8_t* codes, void* scales, hipStream_t stream);

@@ -59,6 +59,26 @@ def test_sort_rejects(lib):
     assert B.moe_sort_capacity(64, 4, 32, 16) == 64 * 4 + 32 * 15
 
 
+def test_route_align_rejects(lib):
+    """Validation of the fused router + sort call happens on the host, before any launch."""
+    P = ctypes.c_void_p
+    f = lambda *a: lib.moe_route_align(*a)
+    ok = [P(FAKE), 4, 8, 2, 0, 1, 0, 1.0, 16] + [P(FAKE)] * 7 + [None]
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert with_(1, -1) == B.MOE_EINVAL                 # T < 0
+    assert with_(3, 9) == B.MOE_EINVAL                  # topk > E
+    assert with_(4, 5) == B.MOE_EINVAL                  # unknown score
+    assert with_(8, 24) == B.MOE_EINVAL                 # block_m
+    assert with_(0, None) == B.MOE_EINVAL               # logits NULL with T > 0
+    assert with_(11, None) == B.MOE_EINVAL              # expert_counts NULL
+    a = list(ok); a[2] = 1000; a[6] = 30
+    assert f(*a) == B.MOE_EINVAL                        # E + n_shared > 1024
+    assert "moe_route_align" in B.moe_last_error()
+
+
 def test_quant_rejects(lib):
     P = ctypes.c_void_p
     assert lib.moe_quant_act(P(FAKE), 4, 100, B.A_FP8_G128, P(FAKE), P(FAKE), None) == B.MOE_EINVAL

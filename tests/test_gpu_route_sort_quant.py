@@ -55,6 +55,39 @@ def test_route_empty():
     assert ids.shape == (0, 2)
 
 
+ROUTE_ALIGN_CASES = [
+    # T, E, topk, score, renorm, n_shared, bm   (fused when E <= 64, T*(topk+n_shared) <= 4096, T*E <= 8192)
+    (64, 32, 4, "softmax", True, 0, 16), (1, 8, 2, "softmax", True, 0, 16), (0, 32, 4, "softmax", True, 0, 16),
+    (32, 256, 8, "sigmoid", True, 1, 16), (8, 992, 32, "softmax", False, 32, 16), (1024, 8, 2, "softmax", True, 0, 32),
+    (455, 256, 8, "sigmoid", True, 1, 32), (1024, 128, 4, "softmax", True, 0, 64), (37, 992, 32, "softmax", True, 32, 128),
+    (100, 96, 3, "softmax", False, 2, 16), (1025, 128, 4, "softmax", True, 0, 64), (8192, 128, 4, "softmax", True, 0, 128),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_ALIGN_CASES)
+def test_route_align(case):
+    """The fused call equals route + sort run separately, bit for bit, and the oracle."""
+    T, E, k, score, renorm, ns, bm = case
+    say(f"route_align T={T} E={E} k={k} {score} renorm={renorm} shared={ns} bm={bm} fused={E <= 64 and T * (k + ns) <= 4096 and T * E <= 8192}")
+    logits = make_logits(T, E, "normal", 500 + T + E)
+    sw = 0.5 if ns else 1.0
+    lg = to_dev(logits)
+    ids, w, srt = B.moe_route_align(lg, k, bm, score, renorm, ns, sw)
+    ids2, w2 = B.moe_route_topk(lg, k, score, renorm, ns, sw)
+    srt2 = B.moe_align_sort(ids2, E + ns, bm)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    for key in ("expert_counts", "expert_offsets", "sorted_slots", "block_expert", "num_padded"):
+        assert torch.equal(srt[key], srt2[key]), key
+    ref_ids, _ = orc.route_topk(logits, k, orc.SCORE_SOFTMAX if score == "softmax" else orc.SCORE_SIGMOID, renorm,
+                                ns, sw)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = orc.align_sort(ref_ids, E + ns, bm)
+    for key in ("expert_counts", "expert_offsets", "sorted_slots"):
+        assert np.array_equal(srt[key].cpu().numpy(), ref[key]), key
+    assert int(srt["num_padded"].cpu()[0]) == ref["num_padded"]
+
+
 SORT_CASES = [(64, 2, 8, 16), (64, 4, 32, 16), (64, 4, 32, 32), (8192, 4, 128, 128), (8192, 4, 128, 64),
               (4096, 9, 257, 128), (1, 2, 8, 16), (16, 2, 8, 16), (256, 2, 8, 64), (4096, 2, 8, 128),
               (1000, 5, 1024, 16), (0, 4, 32, 16), (20000, 3, 7, 32)]
