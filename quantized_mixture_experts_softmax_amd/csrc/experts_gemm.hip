@@ -690,21 +690,12 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
   }
 }
 
-// ---------------------------------------------------------------------------------
-// Stream kernel (16-row blocks whose activation tile fits in LDS: the decode shape).
-// The block's whole activation tile (16 rows x K, gathered token rows in stage 1) is
-// loaded into LDS once; then each of the WAVES waves streams the full K extent of its
-// own NT weight tiles from HBM straight into registers, D chunks ahead of the MFMAs,
-// reading its A operands from LDS.  Waves own disjoint output columns, so there is no
-// barrier and no cross-wave reduction after the tile load.  Compared with each wave
-// fetching its activation fragments from L2, this reads the activations once per
-// workgroup, which is what keeps a 4-bit weight stream (whose activations are four
-// times as many bytes per row) at HBM speed.
 template <int AF>
 constexpr int a_bytes_x2() { return AF == kABf16 ? 4 : (AF == kAMxfp4 ? 1 : 2); }  // 2 x bytes per element
 
-// LDS bytes of the stream kernel's activation tile, row table and scales, rounded to 16.
-__host__ __device__ inline size_t stream_lds_tile_bytes(int afmt, int K) {
+// LDS bytes of a 16-row activation tile (rows padded to whole 128-K chunks, 16 B row
+// skew), its row table and its scales, rounded to 16.
+__host__ __device__ inline size_t tile16_lds_bytes(int afmt, int K) {
   const int nch = (K + 127) / 128;
   const size_t pad_bytes = (size_t)nch * ((afmt == kABf16) ? 256 : (afmt == kAMxfp4 ? 64 : 128));
   size_t sc = 0;
@@ -712,263 +703,6 @@ __host__ __device__ inline size_t stream_lds_tile_bytes(int afmt, int K) {
   if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
   if (afmt == kAFp8Token) sc = 16 * 4;
   return (16 * (pad_bytes + 16) + 64 + sc + 15) / 16 * 16;
-}
-
-template <int STAGE, int WF, int AF, int NT, int D, int WAVES, int KS, int WL>
-__global__ __launch_bounds__(64 * WAVES) void moe_gemm_stream_kernel(const GemmParams p) {
-  using WLay = WLayout<WF, WL>;
-  constexpr int BM = 16;
-  constexpr int NTH = 64 * WAVES;
-  constexpr int NG = WAVES / KS;  // column groups; KS waves (contiguous K ranges) per group
-  static_assert(WAVES % KS == 0, "waves split evenly over K");
-  constexpr int COLS_PER_WAVE = (STAGE == 1) ? 8 * NT : 16 * NT;
-  constexpr int COLS_PER_WG = COLS_PER_WAVE * NG;
-  static_assert(STAGE == 2 || NT % 2 == 0, "stage 1 pairs gate and up tiles");
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const int n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
-  const int G = p.num_blocks * n_tiles;
-  const int lid = xcd_remap((int)blockIdx.x, G);
-  const int b = lid % p.num_blocks;
-  const int nt_idx = lid / p.num_blocks;
-  const int e = p.block_expert[b];  // num_blocks entries, -1 past the end
-  if (e < 0 || b * BM >= p.num_padded[0]) return;
-
-  const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int wv = tid >> 6, w = wv % NG, kp = wv / NG;  // column group, K part
-  const int K = p.K, nch = (K + 127) / 128;
-  const int cpk = (nch + KS - 1) / KS;                 // chunk slots per K part
-  const int c_begin = kp * cpk;
-  const int n_loc = max(0, min(nch, c_begin + cpk) - c_begin);
-  const int TK = p.T * p.slots_per_token;
-  const int row_bytes = K * a_bytes_x2<AF>() / 2;          // A bytes per row in memory
-  const int pad_bytes = nch * 128 * a_bytes_x2<AF>() / 2;   // row padded to whole chunks (zero tail)
-  const int lrow = pad_bytes + 16;                          // padded LDS row
-  const int ngp = nch * 4;                                  // MXFP4 scale bytes per LDS row (zero tail)
-  uint8_t* lds_a = smem;                                    // [16][lrow]
-  int* lds_row = (int*)(smem + BM * lrow);                  // [16] A row index, -1 = pad
-  uint8_t* lds_sc = smem + BM * lrow + 64;                  // A scales: [16][nch] f32 | [16][ngp] u8 | [16] f32
-
-  // ---- this wave's weight tiles ----
-  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
-  const int nbn = (p.Nw + 127) / 128, nbk = nch;
-  const uint8_t* w_src[NT];
-  const uint8_t* ws_src[NT];
-  const float* wsb_src[NT];
-  int col[NT];
-  bool col_ok[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int c, trow;
-    if (STAGE == 1) {
-      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + (t % (NT / 2)) * 16 + li;
-      col_ok[t] = c < p.N;
-      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
-    } else {
-      c = nt_idx * COLS_PER_WG + w * COLS_PER_WAVE + t * 16 + li;
-      col_ok[t] = c < p.N;
-      trow = col_ok[t] ? c - li : 0;
-    }
-    col[t] = c;
-    w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
-    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
-    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
-  }
-
-  // j = chunk slot of this wave's K part; slots past its range read the zero page
-  auto load_w = [&](int j, WeightRegs<WF, NT>& r) {
-    const bool live = j < n_loc;
-    const int cc = min(nch - 1, c_begin + (live ? j : max(n_loc - 1, 0)));
-    const bool kok = live && (cc * 128 + 32 * g < K);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if constexpr (WF == kWMxfp4) {
-        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
-        r.s[t] = ld8(ws_src[t], (size_t)cc * WLay::kScaleStride, kok);
-      } else {
-        r.w[t][0] = ld16(w_src[t], (size_t)cc * WLay::kDataStride, kok);
-        r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)cc * WLay::kDataStride + WLay::kHiOff, kok);
-        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)cc, live);
-      }
-    }
-  };
-
-  // The first D weight chunks do not depend on the activation tile: start streaming
-  // them before the tile is loaded so HBM is busy from the first cycle.
-  WeightRegs<WF, NT> ring[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_w(d, ring[d]);
-
-  // ---- activation tile -> LDS ----
-  if (tid < BM) {
-    int arow = b * BM + tid;
-    if (STAGE == 1) {
-      const int slot = p.sorted_slots[arow];
-      arow = slot < TK ? slot / p.slots_per_token : -1;
-    }
-    lds_row[tid] = arow;
-  }
-  __syncthreads();
-  {
-    const int ppr = pad_bytes / 16;  // 16 B pieces per LDS row; those past the row's bytes are zero
-    for (int q = tid; q < BM * ppr; q += NTH) {
-      const int r = q / ppr, pc = q % ppr;
-      const int arow = lds_row[r];
-      const bool ok = arow >= 0 && 16 * pc < row_bytes;
-      const i32x4 v = ld16((const uint8_t*)p.a, (size_t)(arow < 0 ? 0 : arow) * row_bytes + 16 * pc, ok);
-      *(i32x4*)(lds_a + r * lrow + 16 * pc) = v;
-    }
-    if constexpr (AF == kAFp8G128) {
-      for (int q = tid; q < BM * nch; q += NTH) {
-        const int r = q / nch, c = q % nch, arow = lds_row[r];
-        ((float*)lds_sc)[q] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * nch + c, arow >= 0);
-      }
-    } else if constexpr (AF == kAMxfp4) {
-      const int ng = K / 32;
-      for (int q = tid; q < BM * ngp; q += NTH) {
-        const int r = q / ngp, c = q % ngp, arow = lds_row[r];
-        lds_sc[q] = (uint8_t)ld8((const uint8_t*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * ng + c, arow >= 0 && c < ng);
-      }
-    } else if constexpr (AF == kAFp8Token) {
-      if (tid < BM) {
-        const int arow = lds_row[tid];
-        ((float*)lds_sc)[tid] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
-      }
-    }
-  }
-  __syncthreads();
-
-  f32x4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int j, const WeightRegs<WF, NT>& wr) {
-    // Past the wave's range the weights are zero (zero-page loads); reading a valid
-    // activation chunk keeps the operands finite, so those MFMAs add exactly zero and the
-    // loop stays branch-free.
-    const int c = min(nch - 1, c_begin + min(j, max(n_loc - 1, 0)));
-    const uint8_t* arow = lds_a + li * lrow;
-    if constexpr (AF == kABf16) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 af = *(const bf16x8*)(arow + 256 * c + 64 * g + 16 * st);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float sc = e8m0_to_f32(wr.s[t]);
-          const uint32_t dw = (uint32_t)wr.w[t][0][st];
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
-          const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[t], 0, 0, 0);
-        }
-      }
-    } else if constexpr (AF == kAMxfp4) {
-      const i32x4 a4 = *(const i32x4*)(arow + 64 * c + 16 * g);
-      const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
-      const int sa = (int)lds_sc[li * ngp + 4 * c + g];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const i32x8 b8 = {wr.w[t][0][0], wr.w[t][0][1], wr.w[t][0][2], wr.w[t][0][3], 0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, sa, 0, (int)wr.s[t]);
-      }
-    } else {
-      const i32x4 lo = *(const i32x4*)(arow + 128 * c + 32 * g);
-      const i32x4 hi = *(const i32x4*)(arow + 128 * c + 32 * g + 16);
-      const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      float asr[4];
-      if constexpr (WF == kWFp8Block) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) asr[rr] = ((const float*)lds_sc)[(4 * g + rr) * nch + c];
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const i32x4 wl = wr.w[t][0], wh = wr.w[t][WF == kWMxfp4 ? 0 : 1];
-        const i32x8 b8 = {wl[0], wl[1], wl[2], wl[3], wh[0], wh[1], wh[2], wh[3]};
-        if constexpr (WF == kWFp8Block) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                              0, 127, 0, 127);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) acc[t][rr] += part[rr] * (asr[rr] * wr.sb[t]);
-        } else {
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 0, 0, 0, 127, 0, 127);
-        }
-      }
-    }
-  };
-
-  // D-deep register ring: chunk c lives in ring[c % D]; the loop is unrolled by D so
-  // every ring index is a compile-time constant.  sched_barrier keeps the prefetch of
-  // chunk c + D from being sunk below the MFMAs of chunk c.
-  for (int c0 = 0; c0 < cpk; c0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      __builtin_amdgcn_sched_barrier(0);
-      compute(c0 + d, ring[d]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(c0 + d + D, ring[d]);
-    }
-  }
-
-  // K parts 1..KS-1 hand their partial sums to part 0 through LDS; part 0 adds them in
-  // part order (deterministic) and runs the epilogue.
-  if constexpr (KS > 1) {
-    float* red = (float*)(smem + stream_lds_tile_bytes(AF, K));  // [KS-1][NG][NT*4][64]
-    if (kp > 0) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) red[(((kp - 1) * NG + w) * NT * 4 + t * 4 + rr) * 64 + lane] = acc[t][rr];
-    }
-    __syncthreads();
-    if (kp > 0) return;
-#pragma unroll
-    for (int q = 1; q < KS; ++q)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[t][rr] += red[(((q - 1) * NG + w) * NT * 4 + t * 4 + rr) * 64 + lane];
-  }
-
-  // ---- epilogue: this wave's columns ----
-  if constexpr (STAGE == 1) {
-#pragma unroll
-    for (int t = 0; t < NT / 2; ++t) {
-      if (!col_ok[t]) continue;
-      const int tu = t + NT / 2;
-      const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col[t]] : 1.0f;
-      const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col[t]] : 1.0f;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * g + rr;
-        float gv = acc[t][rr], uv = acc[tu][rr];
-        if constexpr (WF == kWFp8Channel) {
-          const float as = ((const float*)lds_sc)[row];
-          gv = gv * as * wg;
-          uv = uv * as * wu;
-        }
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(hv);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 4 * g + rr;
-      const int slot = p.sorted_slots[b * BM + row];
-      if (slot >= TK) continue;
-      const float tw = p.topk_weights[slot];
-      const float as = (WF == kWFp8Channel) ? ((const float*)lds_sc)[row] : 1.0f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (!col_ok[t]) continue;
-        float v = acc[t][rr];
-        if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col[t]];
-        p.ybuf[(size_t)slot * p.N + col[t]] = v * tw;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1010,7 +744,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   uint8_t* lds_a = smem;
   int* lds_row = (int*)(smem + BM * lrow);
   uint8_t* lds_sc = smem + BM * lrow + 64;
-  float* lds_part = (float*)(smem + stream_lds_tile_bytes(AF, K));  // [WAVES][NT*4][64]
+  float* lds_part = (float*)(smem + tile16_lds_bytes(AF, K));  // [WAVES][NT*4][64]
 
   const size_t nbn = (size_t)(p.Nw + 127) / 128;
 
@@ -1251,12 +985,6 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   }
 }
 
-// LDS bytes of the stream kernel: activation tile, row table and scales (16 B aligned),
-// then the cross-part reduction area.
-static size_t stream_lds_bytes(int afmt, int K, int ks, int ng, int nt) {
-  return stream_lds_tile_bytes(afmt, K) + (size_t)(ks - 1) * ng * nt * 4 * 64 * 4;
-}
-
 // out[t, :] = bf16( sum_{j ascending} ybuf[t*K + j, :] ), slots with invalid ids skipped.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf, const int32_t* __restrict__ ids,
                                                       int T, int K, int H, int E, uint16_t* __restrict__ out) {
@@ -1276,22 +1004,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *(uint2*)(out + (size_t)t * H + c) = make_uint2(lo, hi);
 }
 
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 4
-#endif
-#ifndef MOE_STREAM_DEPTH
-#define MOE_STREAM_DEPTH 3
-#endif
-#ifndef MOE_STREAM_WAVES
-#define MOE_STREAM_WAVES 8
-#endif
-#ifndef MOE_STREAM_KSPLIT
-#define MOE_STREAM_KSPLIT 1
-#endif
-constexpr size_t kStreamLdsMax = 128 * 1024;
-#ifndef MOE_BM16_PERSIST
-#define MOE_BM16_PERSIST 1
-#endif
+constexpr size_t kPersistLdsMax = 128 * 1024;  // dynamic LDS the persistent kernel may use
 #ifndef MOE_PERSIST_WAVES
 #define MOE_PERSIST_WAVES 16
 #endif
@@ -1319,7 +1032,7 @@ static int device_cus() {
 
 // LDS bytes of the persistent kernel: activation tile + one partial-sum slot per wave.
 static size_t persist_lds_bytes(int afmt, int K, int waves) {
-  return stream_lds_tile_bytes(afmt, K) + (size_t)waves * 2 * 4 * 64 * 4;
+  return tile16_lds_bytes(afmt, K) + (size_t)waves * 2 * 4 * 64 * 4;
 }
 
 template <int STAGE, int WF, int AF, int WL>
@@ -1330,7 +1043,7 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
   auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPersistLdsMax);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1345,36 +1058,11 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
   return hipGetLastError();
 }
 
-template <int STAGE, int WF, int AF, int WL>
-static hipError_t launch_stream(const GemmParams& p, size_t lds, hipStream_t stream) {
-  constexpr int NT = MOE_STREAM_NT, D = MOE_STREAM_DEPTH, WAVES = MOE_STREAM_WAVES, KS = MOE_STREAM_KSPLIT;
-  constexpr int COLS_PER_WG = ((STAGE == 1) ? 8 * NT : 16 * NT) * (WAVES / KS);
-  const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
-  const long G = (long)p.num_blocks * n_tiles;
-  if (G == 0) return hipSuccess;
-  if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  auto kern = moe_gemm_stream_kernel<STAGE, WF, AF, NT, D, WAVES, KS, WL>;
-  static bool attr_set = false;  // raise the dynamic LDS limit once per process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  kern<<<(unsigned)G, 64 * WAVES, lds, stream>>>(p);
-  return hipGetLastError();
-}
-
 template <int STAGE, int WF, int AF, int BM, int WL>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
-    if (MOE_BM16_PERSIST) {
-      const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
-      if (lds <= kStreamLdsMax) return launch_persist<STAGE, WF, AF, WL>(p_in, lds, stream);
-    } else {
-      const size_t lds = stream_lds_bytes(AF, p_in.K, MOE_STREAM_KSPLIT, MOE_STREAM_WAVES / MOE_STREAM_KSPLIT,
-                                          MOE_STREAM_NT);
-      if (lds <= kStreamLdsMax) return launch_stream<STAGE, WF, AF, WL>(p_in, lds, stream);
-    }
+    const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
+    if (lds <= kPersistLdsMax) return launch_persist<STAGE, WF, AF, WL>(p_in, lds, stream);
   }
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;
