@@ -127,7 +127,9 @@ struct WLayout {
 };
 
 template <int STAGE, int WF, int AF, int BM, int NT, int WL>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
+// 64-row blocks: the register budget keeps two waves per SIMD resident (measured: up to
+// 1.8x faster than one); 128-row blocks would spill under that budget.
+__global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int ARB = (AF == kABf16) ? 256 : (AF == kAMxfp4 ? 64 : 128);  // A bytes per row per chunk
   constexpr int APC = ARB / 16;                                            // 16 B pieces per row per chunk
@@ -230,11 +232,12 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
     for (int it = 0; it < AIT; ++it)
       reg[it] = ld16(a_src[it], (size_t)c * ARB, a_ok[it] && (c * 128 + a_k0[it] < K));
   };
+  // (chunks past the end, which the ring loop prefetches, read the zero page)
   auto load_as = [&](int c, float& fs, uint32_t& qs) {
     if constexpr (AF == kAFp8G128) {
-      fs = ldf((const float*)p.a_scale, (size_t)s_row * nch + c, s_ok);
+      fs = ldf((const float*)p.a_scale, (size_t)s_row * nch + (c < nch ? c : 0), s_ok && c < nch);
     } else if constexpr (AF == kAMxfp4) {
-      const uint8_t* sp = (const uint8_t*)p.a_scale + (size_t)s_row * (K / 32) + c * 4;
+      const uint8_t* sp = (const uint8_t*)p.a_scale + (size_t)s_row * (K / 32) + (c < nch ? c : 0) * 4;
       uint32_t v = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) v |= ld8(sp, q, s_ok && c * 128 + 32 * q < K) << (8 * q);
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
       } else {
         r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
         r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)c * WLay::kDataStride + WLay::kHiOff, kok);
-        if constexpr (WF == kWFp8Block) r.sb[t] = wsb_src[t][c];
+        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)(c < nch ? c : 0), c < nch);
       }
     }
   };
@@ -273,24 +276,8 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
 
   if constexpr (AF == kAFp8Token) if (tid < BM) lds_as[0][tid] = s_ok ? ((const float*)p.a_scale)[s_row] : 0.0f;
 
-  i32x4 areg[AIT];
-  float fs = 0.f;
-  uint32_t qs = 0;
-  WeightRegs<WF, NT> wr, wn;
-  load_a(0, areg);
-  load_as(0, fs, qs);
-  load_w(0, wr);
-  store_a(0, areg, fs, qs);
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more) {
-      load_a(c + 1, areg);
-      load_as(c + 1, fs, qs);
-      load_w(c + 1, wn);
-    }
+  // MFMAs of one chunk: A from LDS buffer buf, weights wr
+  auto compute = [&](int buf, const WeightRegs<WF, NT>& wr) {
     const uint8_t* la = lds_a[buf];
     if constexpr (AF == kABf16) {
       // w4a16: fp4 -> bf16 in registers, 4 K-steps of 8 per chunk
@@ -355,12 +342,81 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmParams p) {
         }
       }
     }
-    if (more) {
-      store_a(buf ^ 1, areg, fs, qs);
-      wr = wn;
+  };
+
+  // Two loop shapes, chosen per format by measurement on MI355X.  kPF == 0: chunk c + 1
+  // is loaded at the top of iteration c (w4a16).  kPF >= 1: a ring where the loads of
+  // chunks c + 1 .. c + kPF are in flight during chunk c's MFMAs, A staged in registers
+  // (slot j % kPF for chunk j) and weights in ring slot j % (kPF + 1); the loop is
+  // unrolled over the ring period so every slot index is a compile-time constant (a
+  // register copy would wait for its load).
+  constexpr int kPF = (AF == kABf16) ? 0 : (WF == kWFp8Channel ? 2 : 1);
+  if constexpr (kPF == 0) {
+    i32x4 areg[AIT];
+    float fs = 0.f;
+    uint32_t qs = 0;
+    WeightRegs<WF, NT> wr, wn;
+    load_a(0, areg);
+    load_as(0, fs, qs);
+    load_w(0, wr);
+    store_a(0, areg, fs, qs);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < nch;
+      if (more) {
+        load_a(c + 1, areg);
+        load_as(c + 1, fs, qs);
+        load_w(c + 1, wn);
+      }
+      compute(buf, wr);
+      if (more) {
+        store_a(buf ^ 1, areg, fs, qs);
+        wr = wn;
+      }
+      __syncthreads();
+    }
+  } else {
+    constexpr int NA = kPF, NW = kPF + 1, U = NA * NW;  // lcm: NA and NA + 1 are coprime
+    i32x4 areg[NA][AIT];
+    float fsq[NA];
+    uint32_t qsq[NA];
+    WeightRegs<WF, NT> wq[NW];
+    {
+      i32x4 a0[AIT];
+      float f0 = 0.f;
+      uint32_t q0 = 0;
+      load_a(0, a0);
+      load_as(0, f0, q0);
+      load_w(0, wq[0]);
+#pragma unroll
+      for (int j = 1; j <= kPF; ++j) {
+        fsq[j % NA] = 0.f;
+        qsq[j % NA] = 0;
+        load_a(j, areg[j % NA]);
+        load_as(j, fsq[j % NA], qsq[j % NA]);
+        load_w(j, wq[j % NW]);
+      }
+      store_a(0, a0, f0, q0);
     }
     __syncthreads();
+    for (int c0 = 0; c0 < nch; c0 += U)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      if (c >= nch) break;
+      // chunk c + kPF goes into the slots chunk c (A, now in LDS) and c - 1 (weights) left
+      fsq[(u + kPF) % NA] = 0.f;
+      qsq[(u + kPF) % NA] = 0;
+      load_a(c + kPF, areg[(u + kPF) % NA]);
+      load_as(c + kPF, fsq[(u + kPF) % NA], qsq[(u + kPF) % NA]);
+      load_w(c + kPF, wq[(u + kPF) % NW]);
+      compute(c & 1, wq[u % NW]);
+      if (c + 1 < nch) store_a((c + 1) & 1, areg[(u + 1) % NA], fsq[(u + 1) % NA], qsq[(u + 1) % NA]);
+      __syncthreads();
+    }
   }
+
 
   // ---- epilogue ----
   if constexpr (STAGE == 1) {

@@ -128,7 +128,7 @@ def test_workspace_layout(lib):
 
 def test_pick_block_m(lib):
     assert B.moe_pick_block_m(64, 4, 32) == 16
-    assert B.moe_pick_block_m(8192, 4, 128) == 128
+    assert B.moe_pick_block_m(8192, 4, 128) == 64  # 128-row blocks run one wave per SIMD
     assert B.moe_pick_block_m(256, 2, 8) == 64
 
 
