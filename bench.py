@@ -14,7 +14,9 @@ done when the weights are loaded, outside the timed region).
 
 Prints ONE JSON line.  `roofline` is for the stage-1 GEMM (the dominant kernel): its
 algorithmic bytes (or flops) per launch divided by its average duration, timed with HIP
-events recorded on the launch stream around every stage-1 launch of the timed steps.
+events recorded on the launch stream around the stage-1 launch of every n-th timed step
+(--event-every, default 10: each event record adds a few microseconds to its step, so
+the other steps run without them).
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -153,6 +155,8 @@ def main() -> int:
                     help="weight layout: the kernel layout prepared once by moe_tile_weights, or canonical")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record the per-stage HIP events on every n-th timed step (each record adds a few us)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -195,19 +199,24 @@ def main() -> int:
     for i in range(args.warmup):
         layers[i % copies](x, logits)
     torch.cuda.synchronize()
-    evs = [[_event(hip) for _ in range(4)] for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    sampled = [s for s in range(args.steps) if s % every == every - 1] or [args.steps - 1]
+    evs = {s: [_event(hip) for _ in range(4)] for s in sampled}
     ev_start, ev_stop = _event(hip), _event(hip)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev).cuda_stream
     t0 = time.perf_counter()
     hip.hipEventRecord(ctypes.c_void_p(ev_start), ctypes.c_void_p(stream))
     for s in range(args.steps):
-        B.moe_profile_events(evs[s])
+        if s in evs:
+            B.moe_profile_events(evs[s])
         layers[s % copies](x, logits)
+        if s in evs:
+            B.moe_profile_events(None)
     hip.hipEventRecord(ctypes.c_void_p(ev_stop), ctypes.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    B.moe_profile_events(None)
+    evs = list(evs.values())
     gpu_ms = _elapsed_ms(hip, ev_start, ev_stop)
     g1 = [_elapsed_ms(hip, e[0], e[1]) for e in evs]
     g2 = [_elapsed_ms(hip, e[1], e[2]) for e in evs]
@@ -237,6 +246,7 @@ def main() -> int:
     roof["alg_bytes_per_launch"] = alg["gemm1_bytes"]
     roof["alg_flops_per_launch"] = alg["gemm1_flops"]
     roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
+    roof["launches_timed"] = len(evs)
 
     result = {
         "metric": METRIC,

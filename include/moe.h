@@ -176,7 +176,8 @@ moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
  * from moe_quant_act, or NULL to quantise inside this call.
  * Rows come from moe_align_sort run with the same T, K, E_total and block_m.
  * The workspace holds the intermediate h, the a1/a2 codes and an fp32 per-slot buffer
- * [T*K, H]; its layout is reported by moe_workspace_layout().
+ * [T*K, H] of unweighted y rows (each product w * y is rounded to fp32 before it is
+ * added); its layout is reported by moe_workspace_layout().
  * Limits: H % 32 == 0, I % 32 == 0, H, I <= 65536, 1 <= K <= 64, E_total <= 1024,
  * block_m in {16, 32, 64, 128}; (wfmt, afmt) one of
  *   (MXFP4, BF16) (MXFP4, MXFP4_G32) (FP8_BLOCK128, FP8_G128) (FP8_CHANNEL, FP8_TOKEN)

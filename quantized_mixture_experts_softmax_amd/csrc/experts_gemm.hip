@@ -4,8 +4,8 @@
 // gate rows and the matching up rows, with h = bf16(silu(gate) * up) in the
 // epilogue (pages: "rocm_aiter_moe", AiterExperts -- SiLU, act-and-mul -- and
 // rocm_aiter_fused_experts; w13 stacks gate rows over up rows).
-// Stage 2: y = A . w2[e]^T, multiplied by the slot's top-k weight and written as
-// fp32 to a per-slot row; the combine kernel then sums each token's slots in
+// Stage 2: y = A . w2[e]^T, written as fp32 to a per-slot row; the combine kernel
+// then multiplies each of a token's rows by the slot's top-k weight and sums them in
 // ascending slot order (the top-k weighted reduction the pages place inside the
 // expert computation: AiterExperts.finalize_weight_and_reduce_impl is a no-op).
 //
@@ -447,14 +447,13 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         const int row = m * 16 + 4 * g + rr;
         const int slot = p.sorted_slots[b * BM + row];
         if (slot >= TK) continue;
-        const float tw = p.topk_weights[slot];
         const float as = (WF == kWFp8Channel) ? lds_as[0][row] : 1.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if (!col_ok[t]) continue;
           float v = acc[m][t][rr];
           if (WF == kWFp8Channel) v = v * as * wsc[t];
-          p.ybuf[(size_t)slot * p.N + col[t]] = v * tw;
+          p.ybuf[(size_t)slot * p.N + col[t]] = v;
         }
       }
   }
@@ -707,7 +706,6 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
             const int row = m * 16 + 4 * g + rr;
             const int slot = p.sorted_slots[b * BM + row];
             if (slot >= TK) continue;
-            const float tw = p.topk_weights[slot];
             const float as = (WF == kWFp8Channel) ? ((const float*)p.a_scale)[b * BM + row] : 1.0f;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -715,7 +713,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
               if (col >= p.N) continue;
               float v = acc[m][t][rr];
               if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
-              p.ybuf[(size_t)slot * p.N + col] = v * tw;
+              p.ybuf[(size_t)slot * p.N + col] = v;
             }
           }
       }
@@ -749,16 +747,47 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
 template <int AF>
 constexpr int a_bytes_x2() { return AF == kABf16 ? 4 : (AF == kAMxfp4 ? 1 : 2); }  // 2 x bytes per element
 
-// LDS bytes of a 16-row activation tile (rows padded to whole 128-K chunks, 16 B row
-// skew), its row table and its scales, rounded to 16.
+// 16-byte units of one activation row per 128-K chunk.
+__host__ __device__ constexpr int a_units_per_chunk(int afmt) {
+  return afmt == kABf16 ? 16 : (afmt == kAMxfp4 ? 4 : 8);
+}
+
+// LDS bytes of a 16-row activation tile (rows padded to whole 128-K chunks), its row
+// tables (row, slot, top-k weight) and its scales, rounded to 256 (direct loads of
+// the fp32 scales write whole 64-lane dword runs).
 __host__ __device__ inline size_t tile16_lds_bytes(int afmt, int K) {
   const int nch = (K + 127) / 128;
-  const size_t pad_bytes = (size_t)nch * ((afmt == kABf16) ? 256 : (afmt == kAMxfp4 ? 64 : 128));
+  const size_t tile = (size_t)16 * nch * a_units_per_chunk(afmt) * 16;
   size_t sc = 0;
   if (afmt == kAFp8G128) sc = 16 * (size_t)nch * 4;
   if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
   if (afmt == kAFp8Token) sc = 16 * 4;
-  return (16 * (pad_bytes + 16) + 64 + sc + 15) / 16 * 16;
+  return (tile + 192 + sc + 255) / 256 * 256;
+}
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt at their maxima, i.e.
+// not waited for).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return ((n > 63 ? 63 : n) & 0xF) | (((n > 63 ? 63 : n) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations,
+// not for its global loads in flight (__syncthreads waits for those too, which would
+// drain the weight prefetch ring).  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS load of 16 bytes per lane: the wave's 64 x 16 bytes land
+// contiguously at dst (wave-uniform).  Counted by vmcnt like any other load.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------
@@ -775,10 +804,26 @@ __host__ __device__ inline size_t tile16_lds_bytes(int afmt, int K) {
 // wave order (a fixed order, so results do not depend on timing).  Compared with one
 // workgroup per column strip, the HBM stream of a CU never drains between strips, and
 // the load is balanced to within one unit per workgroup.
+//
+// Phase start, in issue order: the row table (sorted slots) -> the activation tile by
+// direct global -> LDS loads -> the first D weight steps of the ring.  Loads complete
+// in issue order, so one wait for "at most D steps' loads outstanding" means the tile
+// has landed while the weights keep streaming; the MFMAs start as soon as the first
+// ring step arrives.  (A plain __syncthreads here would wait for the whole ring.)  The
+// tile is XOR-swizzled: 16-byte unit u of row r sits at unit u ^ (r mod units per
+// chunk), so the fragment reads of the 16 rows spread over the LDS banks although each
+// direct load writes 1 KB contiguously.
 template <int STAGE, int WF, int AF, int D, int WAVES, int WL>
 __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int BM = 16, NT = 2;
+  constexpr int SEG = a_units_per_chunk(AF);
+  // vector-memory instructions of one ring step (load_next): per tile, the 16 B code
+  // piece(s) and the E8M0 byte (MXFP4) or the fp32 block / channel scale (FP8)
+  constexpr int kStepLoads = NT * (WF == kWMxfp4 ? 2 : 3);
+  constexpr int kRingLoads = D * kStepLoads;
+  static_assert(kRingLoads <= 63, "vmcnt range");
+  constexpr int kThreads = 64 * WAVES;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -794,13 +839,15 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
 
   const int TK = p.T * p.slots_per_token;
   const int row_bytes = K * a_bytes_x2<AF>() / 2;
-  const int pad_bytes = nch * 128 * a_bytes_x2<AF>() / 2;
-  const int lrow = pad_bytes + 16;
+  const int upr = nch * SEG;   // 16-byte units per tile row
+  const int n_dma = upr / 4;   // 64-lane direct loads per tile (16 rows x upr units)
   const int ngp = nch * 4;
   uint8_t* lds_a = smem;
-  int* lds_row = (int*)(smem + BM * lrow);
-  uint8_t* lds_sc = smem + BM * lrow + 64;
+  int* lds_row = (int*)(smem + (size_t)16 * upr * 16);  // activation row of each tile row (-1: pad)
+  int* lds_slot = lds_row + 16;                          // sorted slot of each tile row
+  uint8_t* lds_sc = (uint8_t*)(lds_slot + 32);
   float* lds_part = (float*)(smem + tile16_lds_bytes(AF, K));  // [WAVES][NT*4][64]
+  const MOE_GLOBAL uint8_t* zp = (const MOE_GLOBAL uint8_t*)kZeroPage;
 
   const size_t nbn = (size_t)(p.Nw + 127) / 128;
 
@@ -838,6 +885,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
           r.w[t][1] = ld16(src, (size_t)lc * WLay::kDataStride + WLay::kHiOff, ok);
           if constexpr (WF == kWFp8Block)
             r.sb[t] = ldf((const float*)p.w_scale, ((size_t)e * nbn + trow / 128) * nch + lc, tok);
+          else  // channel scale of the lane's output column, carried with the step
+            r.sb[t] = ldf((const float*)p.w_scale, (size_t)e * p.Nw + trow + li, tok);
         }
       }
       if (live) {
@@ -846,60 +895,87 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
       }
     };
 
-    __syncthreads();  // the previous phase is done with LDS
+    // ---- row table; every wave is done with the previous phase's LDS ----
+    lds_barrier();
+    int slot_v = 0;
+    if (tid < BM) {
+      slot_v = p.sorted_slots[b * BM + tid];
+      if (STAGE == 1) lds_row[tid] = slot_v < TK ? slot_v / p.slots_per_token : -1;
+    }
+    if (STAGE == 1) lds_barrier();
+
+    // activation scales (quantised formats) go through registers, issued before the tile
+    constexpr int kScPer = (AF == kAMxfp4) ? 8 : 1;  // per thread: 16 x 4 x nch bytes <= 8 x kThreads
+    float sc_f = 0.0f;
+    uint32_t sc_b[kScPer];
+    if constexpr (AF == kAFp8G128) {
+      if (tid < BM * nch) {
+        const int r = tid / nch, c = tid % nch;
+        const int arow = STAGE == 1 ? lds_row[r] : b * BM + r;
+        sc_f = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * nch + c, arow >= 0);
+      }
+    } else if constexpr (AF == kAMxfp4) {
+      const int ng = K / 32;
+#pragma unroll
+      for (int i = 0; i < kScPer; ++i) {
+        const int q = tid + kThreads * i;
+        sc_b[i] = 0;
+        if (q < BM * ngp) {
+          const int r = q / ngp, c = q % ngp;
+          const int arow = STAGE == 1 ? lds_row[r] : b * BM + r;
+          sc_b[i] = ld8((const uint8_t*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * ng + c, arow >= 0 && c < ng);
+        }
+      }
+    } else if constexpr (AF == kAFp8Token) {
+      if (tid < BM) {
+        const int arow = STAGE == 1 ? lds_row[tid] : b * BM + tid;
+        sc_f = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
+      }
+    }
+
+    // ---- activation tile -> LDS (direct loads), then the ring ----
+    for (int i = wv; i < n_dma; i += WAVES) {
+      const int v = i * 64 + lane;
+      const int r = v / upr, pv = v - r * upr;
+      const int pu = pv ^ (r & (SEG - 1));  // the unit stored at position pv of row r
+      const int arow = STAGE == 1 ? lds_row[r] : b * BM + r;
+      const bool ok = arow >= 0 && 16 * pu < row_bytes;
+      const MOE_GLOBAL uint8_t* src =
+          ok ? (const MOE_GLOBAL uint8_t*)p.a + (size_t)arow * row_bytes + 16 * pu : zp;
+      dma16((const void*)src, lds_a + (size_t)i * 1024);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     WeightRegs<WF, NT> ring[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) load_next(ring[d]);
-
-    // ---- activation tile -> LDS ----
-    if (tid < BM) {
-      int arow = b * BM + tid;
-      if (STAGE == 1) {
-        const int slot = p.sorted_slots[arow];
-        arow = slot < TK ? slot / p.slots_per_token : -1;
-      }
-      lds_row[tid] = arow;
+    __builtin_amdgcn_sched_barrier(0);
+    // at most the ring's loads outstanding: this wave's tile loads and scales have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRingLoads));
+    if (tid < BM) lds_slot[tid] = slot_v;
+    if constexpr (AF == kAFp8G128) {
+      if (tid < BM * nch) ((float*)lds_sc)[tid] = sc_f;
+    } else if constexpr (AF == kAMxfp4) {
+#pragma unroll
+      for (int i = 0; i < kScPer; ++i)
+        if (tid + kThreads * i < BM * ngp) lds_sc[tid + kThreads * i] = (uint8_t)sc_b[i];
+    } else if constexpr (AF == kAFp8Token) {
+      if (tid < BM) ((float*)lds_sc)[tid] = sc_f;
     }
-    __syncthreads();
-    {
-      const int ppr = pad_bytes / 16;
-      for (int q = tid; q < BM * ppr; q += 64 * WAVES) {
-        const int r = q / ppr, pc = q % ppr;
-        const int arow = lds_row[r];
-        const bool ok = arow >= 0 && 16 * pc < row_bytes;
-        const i32x4 v = ld16((const uint8_t*)p.a, (size_t)(arow < 0 ? 0 : arow) * row_bytes + 16 * pc, ok);
-        *(i32x4*)(lds_a + r * lrow + 16 * pc) = v;
-      }
-      if constexpr (AF == kAFp8G128) {
-        for (int q = tid; q < BM * nch; q += 64 * WAVES) {
-          const int r = q / nch, c = q % nch, arow = lds_row[r];
-          ((float*)lds_sc)[q] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * nch + c, arow >= 0);
-        }
-      } else if constexpr (AF == kAMxfp4) {
-        const int ng = K / 32;
-        for (int q = tid; q < BM * ngp; q += 64 * WAVES) {
-          const int r = q / ngp, c = q % ngp, arow = lds_row[r];
-          lds_sc[q] = (uint8_t)ld8((const uint8_t*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * ng + c, arow >= 0 && c < ng);
-        }
-      } else if constexpr (AF == kAFp8Token) {
-        if (tid < BM) {
-          const int arow = lds_row[tid];
-          ((float*)lds_sc)[tid] = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
-        }
-      }
-    }
-    __syncthreads();
+    lds_barrier();
 
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float csc[NT] = {1.0f, 1.0f};  // FP8 channel: the current unit's column scales
 
+    const int swz = li & (SEG - 1);
     auto compute = [&](int c, const WeightRegs<WF, NT>& wr) {
-      const uint8_t* arow = lds_a + li * lrow;
+      const uint8_t* arow = lds_a + (size_t)li * upr * 16 + (size_t)c * SEG * 16;
       if constexpr (AF == kABf16) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const bf16x8 af = *(const bf16x8*)(arow + 256 * c + 64 * g + 16 * st);
+          const bf16x8 af = *(const bf16x8*)(arow + 16 * ((4 * g + st) ^ swz));
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const float sc = e8m0_to_f32(wr.s[t]);
@@ -913,7 +989,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
           }
         }
       } else if constexpr (AF == kAMxfp4) {
-        const i32x4 a4 = *(const i32x4*)(arow + 64 * c + 16 * g);
+        const i32x4 a4 = *(const i32x4*)(arow + 16 * (g ^ swz));
         const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
         const int sa = (int)lds_sc[li * ngp + 4 * c + g];
 #pragma unroll
@@ -922,8 +998,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
           acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, sa, 0, (int)wr.s[t]);
         }
       } else {
-        const i32x4 lo = *(const i32x4*)(arow + 128 * c + 32 * g);
-        const i32x4 hi = *(const i32x4*)(arow + 128 * c + 32 * g + 16);
+        const i32x4 lo = *(const i32x4*)(arow + 16 * ((2 * g) ^ swz));
+        const i32x4 hi = *(const i32x4*)(arow + 16 * ((2 * g + 1) ^ swz));
         const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         float asr[4];
         if constexpr (WF == kWFp8Block) {
@@ -950,16 +1026,14 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     auto emit = [&](int u) {
       if constexpr (STAGE == 1) {
         const int col = 16 * (ua + u) + li;
-        const float wg_s = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
-        const float wu_s = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int row = 4 * g + rr;
           float gv = acc[0][rr], uv = acc[1][rr];
           if constexpr (WF == kWFp8Channel) {
             const float as = ((const float*)lds_sc)[row];
-            gv = gv * as * wg_s;
-            uv = uv * as * wu_s;
+            gv = gv * as * csc[0];
+            uv = uv * as * csc[1];
           }
           const float hv = gv / (1.0f + __expf(-gv)) * uv;
           p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(hv);
@@ -968,17 +1042,16 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int row = 4 * g + rr;
-          const int slot = p.sorted_slots[b * BM + row];
+          const int slot = lds_slot[row];
           if (slot >= TK) continue;
-          const float tw = p.topk_weights[slot];
           const float as = (WF == kWFp8Channel) ? ((const float*)lds_sc)[row] : 1.0f;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const int col = 32 * (ua + u) + 16 * t + li;
             if (col >= p.N) continue;
             float v = acc[t][rr];
-            if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
-            p.ybuf[(size_t)slot * p.N + col] = v * tw;
+            if constexpr (WF == kWFp8Channel) v = v * as * csc[t];
+            p.ybuf[(size_t)slot * p.N + col] = v;
           }
         }
       }
@@ -995,6 +1068,12 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
         const int j = j0 + d;
         __builtin_amdgcn_sched_barrier(0);
         compute(cc, ring[d]);  // past the run the weights are zero: adds exact zeros
+        if constexpr (WF == kWFp8Channel) {
+          if (j < n) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) csc[t] = ring[d].sb[t];
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
         load_next(ring[d]);
         if (j < n) {
@@ -1022,7 +1101,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
         }
       }
     }
-    __syncthreads();  // partials of shared units are in LDS
+    lds_barrier();  // partials of shared units are in LDS
     if (tail_open) {
       const int u_end = (cu + 1) * nch;  // first step past the open unit
       for (int q = wv + 1; q < WAVES; ++q) {
@@ -1041,9 +1120,13 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   }
 }
 
-// out[t, :] = bf16( sum_{j ascending} ybuf[t*K + j, :] ), slots with invalid ids skipped.
+// out[t, :] = bf16( sum_{j ascending} w[t, j] * ybuf[t*K + j, :] ), slots with invalid
+// ids skipped.  Each product is rounded to fp32 before it is added (no fused
+// multiply-add), the same arithmetic as weighting each row first and summing after.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf, const int32_t* __restrict__ ids,
-                                                      int T, int K, int H, int E, uint16_t* __restrict__ out) {
+                                                      const float* __restrict__ wts, int T, int K, int H, int E,
+                                                      uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
   const int per_row = H / 4;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)T * per_row) return;
@@ -1052,8 +1135,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < K; ++j) {
     const int e = ids[(size_t)t * K + j];
     if (e < 0 || e >= E) continue;
+    const float w = wts[(size_t)t * K + j];
     const f32x4 y = *(const f32x4*)(ybuf + ((size_t)t * K + j) * H + c);
-    acc += y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float prod = y[i] * w;
+      acc[i] = acc[i] + prod;
+    }
   }
   const uint32_t lo = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
   const uint32_t hi = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
@@ -1210,11 +1298,12 @@ hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmPar
   return stage == 1 ? launch_stage<1>(wfmt, afmt, block_m, p, stream) : launch_stage<2>(wfmt, afmt, block_m, p, stream);
 }
 
-hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, int T, int K, int H, int E_total,
-                          uint16_t* out, hipStream_t stream) {
+hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, const float* topk_weights, int T, int K,
+                          int H, int E_total, uint16_t* out, hipStream_t stream) {
   const long n = (long)T * (H / 4);
   if (n == 0) return hipSuccess;
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(ybuf, topk_ids, T, K, H, E_total, out);
+  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(ybuf, topk_ids, topk_weights, T, K, H, E_total,
+                                                                   out);
   return hipGetLastError();
 }
 

@@ -339,7 +339,7 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   if ((e = prof_mark(2, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
 
   // ordered top-k combine
-  e = moe::launch_combine(ybuf, a->topk_ids, a->T, a->K, a->H, a->E_total, a->out, stream);
+  e = moe::launch_combine(ybuf, a->topk_ids, a->topk_weights, a->T, a->K, a->H, a->E_total, a->out, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: combine");
   return hip_status(prof_mark(3, stream), "moe_experts_forward: profiling event");
 }

@@ -52,7 +52,7 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
 hipError_t launch_tile_weights(int wfmt, int E, int N, int K, const uint8_t* w, const void* ws, uint8_t* out,
                                hipStream_t stream);
 hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmParams& p, hipStream_t stream);
-hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, int T, int K, int H, int E_total,
-                          uint16_t* out, hipStream_t stream);
+hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, const float* topk_weights, int T, int K,
+                          int H, int E_total, uint16_t* out, hipStream_t stream);
 
 }  // namespace moe

@@ -53,17 +53,18 @@ def score_name(w: synth.Workload) -> str:
 
 
 def combine_f32(res: dict, tokens: np.ndarray, K: int, H: int, E_total: int) -> np.ndarray:
-    """The GPU's fp32 result before its final bf16 rounding, rebuilt from the weighted
-    per-slot rows it left in the workspace by summing them in the combine kernel's
-    order (ascending slot, fp32)."""
+    """The GPU's fp32 result before its final bf16 rounding, rebuilt from the per-slot
+    rows it left in the workspace the way the combine kernel sums them: in ascending
+    slot order, each row times its top-k weight rounded to fp32, then added in fp32."""
     ybuf = res["ybuf_dev"]
-    ids = res["ids"]
+    ids, wts = res["ids"], res["weights"].astype(np.float32)
     rows = (tokens[:, None] * K + np.arange(K)[None, :]).reshape(-1)
     y = ybuf[torch.from_numpy(rows).to(ybuf.device)].cpu().numpy().reshape(len(tokens), K, H)
     acc = np.zeros((len(tokens), H), np.float32)
     for j in range(K):
         ok = (ids[tokens, j] >= 0) & (ids[tokens, j] < E_total)
-        acc = np.where(ok[:, None], acc + y[:, j], acc).astype(np.float32)
+        prod = (y[:, j] * wts[tokens, j][:, None]).astype(np.float32)
+        acc = np.where(ok[:, None], acc + prod, acc).astype(np.float32)
     return acc
 
 
