@@ -215,6 +215,102 @@ int orc_route_topk(const float* logits, int T, int E, int topk, int score, int r
   return 0;
 }
 
+/* Grouped top-k routing with a score-correction bias.  The pages name this router
+ * only through its parameters (num_expert_group, topk_group, e_score_correction_bias,
+ * routed_scaling_factor, passed to the monolithic kernel in [mxfp4.py]
+ * Mxfp4MoEMethod.apply_monolithic and [quark_moe] QuarkMoEMethod.apply_monolithic)
+ * and through its output buffer ([rocm_aiter_moe] inject_shared_expert_weights: the
+ * grouped router already returns the combined routed + shared buffer).  Reading (the
+ * published group-limited routing of the DeepSeek-V2/V3 models these parameters come
+ * from), per token:
+ *   s[e]   = sigmoid(l[e]), or the softmax of the whole logit row;
+ *   key[e] = s[e] + bias[e] with a bias, else the logit itself (same order as s);
+ *   experts form num_expert_group contiguous groups of E / num_expert_group; a
+ *   group's score is the sum of its two largest keys with a bias, else its largest;
+ *   the topk_group best groups are kept, and the topk best keys among their experts
+ *   are the routed slots, best first (equal keys or group scores: lower id first);
+ *   weight[j] = s[id_j], divided by the sum over the k slots (slot order) when
+ *   renormalising, then times routed_scaling_factor.
+ * Keys, group scores and weights are evaluated in fp64.  Shared slots follow as in
+ * orc_route_topk. */
+int orc_route_grouped_topk(const float* logits, const float* bias, int T, int E, int topk, int n_group,
+                           int topk_group, int score, int renormalize, float scaling, int n_shared,
+                           float shared_weight, int32_t* topk_ids, float* topk_weights) {
+  if (T < 0 || E <= 0 || topk <= 0 || n_shared < 0 || n_group <= 0 || E % n_group != 0) return -1;
+  if (topk_group <= 0 || topk_group > n_group || topk > topk_group * (E / n_group)) return -1;
+  if (score != ORC_SCORE_SOFTMAX && score != ORC_SCORE_SIGMOID) return -1;
+  const int KP = topk + n_shared, gs = E / n_group;
+  double* s = (double*)malloc(sizeof(double) * (size_t)E);
+  double* key = (double*)malloc(sizeof(double) * (size_t)E);
+  double* gsc = (double*)malloc(sizeof(double) * (size_t)n_group);
+  int* gsel = (int*)malloc(sizeof(int) * (size_t)n_group);
+  int* taken = (int*)malloc(sizeof(int) * (size_t)E);
+  if (!s || !key || !gsc || !gsel || !taken) {
+    free(s); free(key); free(gsc); free(gsel); free(taken);
+    return -1;
+  }
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    if (score == ORC_SCORE_SIGMOID) {
+      for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+    } else {
+      double m = (double)l[0], z = 0.0;
+      for (int e = 1; e < E; ++e) if ((double)l[e] > m) m = (double)l[e];
+      for (int e = 0; e < E; ++e) z += exp((double)l[e] - m);
+      for (int e = 0; e < E; ++e) s[e] = exp((double)l[e] - m) / z;
+    }
+    for (int e = 0; e < E; ++e) key[e] = bias ? s[e] + (double)bias[e] : (double)l[e];
+    /* group scores */
+    for (int g = 0; g < n_group; ++g) {
+      const double* kg = key + (size_t)g * gs;
+      int b1 = 0;
+      for (int i = 1; i < gs; ++i) if (kg[i] > kg[b1]) b1 = i;
+      double v = kg[b1];
+      if (bias && gs > 1) {
+        int b2 = -1;
+        for (int i = 0; i < gs; ++i) {
+          if (i == b1) continue;
+          if (b2 < 0 || kg[i] > kg[b2]) b2 = i;
+        }
+        v += kg[b2];
+      }
+      gsc[g] = v;
+      gsel[g] = 0;
+    }
+    for (int r = 0; r < topk_group; ++r) {
+      int best = -1;
+      for (int g = 0; g < n_group; ++g) {
+        if (gsel[g]) continue;
+        if (best < 0 || gsc[g] > gsc[best]) best = g; /* strict: equal scores keep the lower id */
+      }
+      gsel[best] = 1;
+    }
+    /* experts of the kept groups */
+    for (int e = 0; e < E; ++e) taken[e] = !gsel[e / gs];
+    double denom = 0.0;
+    for (int j = 0; j < topk; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || key[e] > key[best]) best = e;
+      }
+      taken[best] = 1;
+      topk_ids[(size_t)t * KP + j] = best;
+      denom += s[best];
+    }
+    for (int j = 0; j < topk; ++j) {
+      const double w = s[topk_ids[(size_t)t * KP + j]];
+      topk_weights[(size_t)t * KP + j] = (float)((renormalize ? w / denom : w) * (double)scaling);
+    }
+    for (int q = 0; q < n_shared; ++q) {
+      topk_ids[(size_t)t * KP + topk + q] = E + q;
+      topk_weights[(size_t)t * KP + topk + q] = shared_weight;
+    }
+  }
+  free(s); free(key); free(gsc); free(gsel); free(taken);
+  return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Token -> expert sort                                                       */
 /* ------------------------------------------------------------------------- */

@@ -45,6 +45,9 @@ int orc_mx_shared_exp(float amax);           /* floor(log2 amax) - 2 clamped to 
 /* ---- router ---- */
 int orc_route_topk(const float* logits, int T, int E, int topk, int score, int renormalize,
                    int n_shared, float shared_weight, int32_t* topk_ids, float* topk_weights);
+int orc_route_grouped_topk(const float* logits, const float* bias, int T, int E, int topk, int n_group,
+                           int topk_group, int score, int renormalize, float scaling, int n_shared,
+                           float shared_weight, int32_t* topk_ids, float* topk_weights);
 
 /* ---- token -> expert sort, padded per expert to block_m rows ---- */
 int64_t orc_sort_capacity(int T, int K, int E_total, int block_m);

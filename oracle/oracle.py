@@ -21,6 +21,12 @@ Which test pins which oracle function (tests/test_oracle_*.py, all CPU):
   orc_route_topk
       brute-force full stable sort; weights sum to 1; top-1 weight exactly 1;
       softmax of the chosen logits equals the renormalised full softmax.
+  orc_route_grouped_topk
+      hand-worked golden examples (tests/golden/grouped_router_examples.txt);
+      one group without bias equals orc_route_topk; the same reading written with
+      numpy sort/lexsort on random inputs with exact ties; slots from at most
+      topk_group groups; weights are the unbiased scores and sum to the scaling
+      factor; a uniform bias shift keeps the ids.
   orc_align_sort
       numpy.argsort(kind="stable") of the flattened ids; offsets multiples of
       block_m; every slot exactly once.
@@ -95,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.orc_mx_shared_exp.argtypes = [ctypes.c_float]
         L.orc_route_topk.restype = I
         L.orc_route_topk.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, P, P]
+        L.orc_route_grouped_topk.restype = I
+        L.orc_route_grouped_topk.argtypes = [P, P, I, I, I, I, I, I, I, ctypes.c_float, I, ctypes.c_float, P, P]
         L.orc_sort_capacity.restype = ctypes.c_int64
         L.orc_sort_capacity.argtypes = [I, I, I, I]
         L.orc_align_sort.restype = I
@@ -174,6 +182,24 @@ def route_topk(logits: np.ndarray, topk: int, score: int = SCORE_SOFTMAX, renorm
                               shared_weight, _ptr(ids), _ptr(w))
     if rc:
         raise ValueError("orc_route_topk: bad arguments")
+    return ids, w
+
+
+def route_grouped_topk(logits: np.ndarray, topk: int, n_group: int, topk_group: int, bias: np.ndarray | None = None,
+                       score: int = SCORE_SIGMOID, renormalize: bool = True, scaling: float = 1.0, n_shared: int = 0,
+                       shared_weight: float = 1.0):
+    """Grouped top-k router with an optional score-correction bias (see
+    orc_route_grouped_topk for the reading of the pages)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    KP = topk + n_shared
+    ids = np.empty((T, KP), np.int32)
+    w = np.empty((T, KP), np.float32)
+    rc = lib().orc_route_grouped_topk(_ptr(logits), _ptr(b), T, E, topk, n_group, topk_group, score,
+                                      int(renormalize), scaling, n_shared, shared_weight, _ptr(ids), _ptr(w))
+    if rc:
+        raise ValueError("orc_route_grouped_topk: bad arguments")
     return ids, w
 
 
