@@ -153,6 +153,8 @@ def main() -> int:
     ap.add_argument("--weight-copies", type=int, default=None)
     ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
                     help="weight layout: the kernel layout prepared once by moe_tile_weights, or canonical")
+    ap.add_argument("--router", choices=["plain", "grouped"], default="plain",
+                    help="grouped: group-limited router (8 groups, 4 kept, seeded correction bias, scaling 2.5)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=10,
@@ -185,13 +187,20 @@ def main() -> int:
     # enough copies that one rotation is larger than twice the Infinity Cache
     copies = args.weight_copies or (1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    grouped = None
+    if args.router == "grouped":
+        if w.E % 8:
+            print("bench.py: --router grouped needs the expert count to split into 8 groups", file=sys.stderr)
+            return 2
+        grouped = dict(num_expert_group=8, topk_group=4, routed_scaling_factor=2.5,
+                       correction_bias=t(synth.make_correction_bias(w)))
     layers = []
     for _ in range(copies):
         layers.append(B.MoELayer(t(data["w1"]), t(data["w1_scale"]), t(data["w2"]), t(data["w2_scale"]), H=w.H,
                                  I=w.I, E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
                                  score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                                  n_shared=w.n_shared, shared_weight=w.shared_weight, block_m=args.block_m,
-                                 tiled=args.layout == "tiled"))
+                                 tiled=args.layout == "tiled", grouped=grouped))
     x = torch.from_numpy(data["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     logits = t(data["logits"])
     hip = _hip()
@@ -266,7 +275,8 @@ def main() -> int:
                    "T": w.T, "H": w.H, "I": w.I, "experts": w.E, "shared_experts": w.n_shared, "topk": w.topk,
                    "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
-                   "weight_layout": args.layout},
+                   "weight_layout": args.layout,
+                   "router_kind": "grouped (8 groups, 4 kept, bias, scaling 2.5)" if grouped else "plain top-k"},
         "roofline": roof,
         "step_breakdown_us": {"gpu_step": round(gpu_ms * 1e3 / args.steps, 2),
                               "stage1_gemm": round(g1_ms * 1e3, 2), "a2_quant+stage2_gemm": round(float(np.mean(g2)) * 1e3, 2),

@@ -103,6 +103,38 @@ moe_status moe_route_topk(const float* router_logits, int T, int E, int topk, mo
                           int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_route_grouped_topk -- group-limited top-k router with a score-correction bias.
+ *
+ * The pages name this router only through the parameters handed to the monolithic
+ * kernel ([mxfp4.py] Mxfp4MoEMethod.apply_monolithic: num_expert_group, topk_group,
+ * e_score_correction_bias, routed_scaling_factor) and its combined routed + shared
+ * output ([rocm_aiter_moe] inject_shared_expert_weights).  Reading (group-limited
+ * routing of the DeepSeek-V2/V3 models these parameters come from), per token t:
+ *   s[e]    = 1 / (1 + exp(-l[e])) (sigmoid) or the softmax of the whole row;
+ *   key[e]  = s[e] + correction_bias[e], or l[e] itself when correction_bias is NULL;
+ *   the E experts form num_expert_group contiguous groups of E / num_expert_group; a
+ *   group's score is the sum of its two largest keys (with a bias) or its largest key;
+ *   the topk_group best groups are kept and the topk best keys among their experts are
+ *   the routed slots, best first; equal keys or group scores: lower id first;
+ *   weight[j] = s[id_j], divided by the sum of the k weights when `renormalize`, then
+ *   multiplied by routed_scaling_factor.
+ * Keys, group scores and weights are computed in fp64 (the ids follow the fp64 order).
+ * Shared slots follow as in moe_route_topk.
+ *   router_logits     [T, E] fp32;  correction_bias [E] fp32 or NULL
+ *   topk_ids          [T, topk + n_shared] int32 (written)
+ *   topk_weights      [T, topk + n_shared] fp32  (written)
+ * Limits: 1 <= E <= 1024; 1 <= num_expert_group <= 64 dividing E; 1 <= topk_group <=
+ * num_expert_group; 1 <= topk <= min(32, topk_group * E / num_expert_group);
+ * 0 <= n_shared <= 32; T >= 0 (T == 0 enqueues nothing).  Logits must be finite.
+ * Errors: MOE_EINVAL for any argument outside these limits, NULL or misaligned pointers.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_route_grouped_topk(const float* router_logits, const float* correction_bias, int T, int E,
+                                  int topk, int num_expert_group, int topk_group, moe_score score,
+                                  int renormalize, float routed_scaling_factor, int n_shared,
+                                  float shared_weight, int32_t* topk_ids, float* topk_weights,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_align_sort -- stable token->expert sort padded to the GEMM row tile.
  *
  * The flattened slots s = t*K + j (K = slots per token, routed + shared) are grouped by
@@ -208,7 +240,7 @@ typedef struct moe_workspace_layout_t {
   size_t h_off, h_bytes;           /* bf16 [cap, I]: stage-1 output in sorted-row order */
   size_t a1_codes_off, a1_codes_bytes, a1_scales_off, a1_scales_bytes; /* quantised hidden_states */
   size_t a2_codes_off, a2_codes_bytes, a2_scales_off, a2_scales_bytes; /* quantised h, sorted rows */
-  size_t ybuf_off, ybuf_bytes;     /* fp32 [T*K, H]: weighted stage-2 rows by slot id */
+  size_t ybuf_off, ybuf_bytes;     /* fp32 [T*K, H]: stage-2 rows (unweighted) by slot id */
   size_t total;
 } moe_workspace_layout_t;
 

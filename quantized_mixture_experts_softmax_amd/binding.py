@@ -21,7 +21,7 @@ A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
 ACT_SILU = 0
 
 EXPORTED = [
-    "moe_route_topk", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
+    "moe_route_topk", "moe_route_grouped_topk", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
     "moe_tiled_weight_bytes", "moe_tile_weights",
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int
         L.moe_route_topk.restype = S
         L.moe_route_topk.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, P, P, P]
+        L.moe_route_grouped_topk.restype = S
+        L.moe_route_grouped_topk.argtypes = [P, P, I, I, I, I, I, I, I, ctypes.c_float, I, ctypes.c_float, P, P, P]
         L.moe_sort_capacity.restype = ctypes.c_size_t
         L.moe_sort_capacity.argtypes = [I, I, I, I]
         L.moe_align_sort.restype = S
@@ -177,6 +179,27 @@ def moe_route_topk(router_logits: torch.Tensor, topk: int, score: str = "softmax
         topk_weights = torch.empty((T, KP), dtype=torch.float32, device=dev)
     _check(lib().moe_route_topk(_ptr(router_logits), T, E, topk, SCORE[score], int(renormalize), n_shared,
                                 shared_weight, _ptr(topk_ids), _ptr(topk_weights), _stream(stream, dev)))
+    return topk_ids, topk_weights
+
+
+def moe_route_grouped_topk(router_logits: torch.Tensor, topk: int, num_expert_group: int, topk_group: int,
+                           correction_bias: torch.Tensor | None = None, score: str = "sigmoid",
+                           renormalize: bool = True, routed_scaling_factor: float = 1.0, n_shared: int = 0,
+                           shared_weight: float = 1.0, topk_ids=None, topk_weights=None, stream=None):
+    dev = _dev(router_logits)
+    assert router_logits.dtype == torch.float32 and router_logits.dim() == 2
+    T, E = router_logits.shape
+    if correction_bias is not None:
+        assert correction_bias.dtype == torch.float32 and correction_bias.numel() == E
+        _dev(correction_bias)
+    KP = topk + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty((T, KP), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, KP), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_grouped_topk(_ptr(router_logits), _ptr(correction_bias), T, E, topk, num_expert_group,
+                                        topk_group, SCORE[score], int(renormalize), routed_scaling_factor, n_shared,
+                                        shared_weight, _ptr(topk_ids), _ptr(topk_weights), _stream(stream, dev)))
     return topk_ids, topk_weights
 
 
@@ -312,8 +335,10 @@ class MoELayer:
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
-                 tiled: bool = False):
-        """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights)."""
+                 tiled: bool = False, grouped: dict | None = None):
+        """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights).
+        grouped = dict(num_expert_group, topk_group, correction_bias (tensor or None),
+        routed_scaling_factor) routes with moe_route_grouped_topk (then moe_align_sort)."""
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
             w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
@@ -327,6 +352,7 @@ class MoELayer:
         self.E_total = E + n_shared
         self.K = topk + n_shared
         self.block_m = block_m
+        self.grouped = grouped
         self._bufs: dict = {}
 
     def _buffers(self, T: int, dev):
@@ -356,8 +382,15 @@ class MoELayer:
     def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
         T = x.shape[0]
         b = self._buffers(T, x.device)
-        moe_route_align(router_logits, self.topk, b["bm"], self.score, True, self.n_shared, self.shared_weight,
-                        b["ids"], b["w"], b["sort"], stream)
+        if self.grouped is None:
+            moe_route_align(router_logits, self.topk, b["bm"], self.score, True, self.n_shared, self.shared_weight,
+                            b["ids"], b["w"], b["sort"], stream)
+        else:
+            g = self.grouped
+            moe_route_grouped_topk(router_logits, self.topk, g["num_expert_group"], g["topk_group"],
+                                   g.get("correction_bias"), self.score, True, g.get("routed_scaling_factor", 1.0),
+                                   self.n_shared, self.shared_weight, b["ids"], b["w"], stream)
+            moe_align_sort(b["ids"], self.E_total, b["bm"], b["sort"], stream)
         a1c = a1s = None
         if self.afmt != A_BF16:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)

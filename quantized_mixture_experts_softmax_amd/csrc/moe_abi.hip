@@ -150,6 +150,31 @@ moe_status moe_route_topk(const float* router_logits, int T, int E, int topk, mo
                     "moe_route_topk launch");
 }
 
+moe_status moe_route_grouped_topk(const float* router_logits, const float* correction_bias, int T, int E, int topk,
+                                  int num_expert_group, int topk_group, moe_score score, int renormalize,
+                                  float routed_scaling_factor, int n_shared, float shared_weight, int32_t* topk_ids,
+                                  float* topk_weights, hipStream_t stream) {
+  const char* fn = "moe_route_grouped_topk";
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "%s: E must be in [1, 1024] (got %d)", fn, E);
+  if (num_expert_group < 1 || num_expert_group > 64 || E % num_expert_group != 0)
+    return fail(MOE_EINVAL, "%s: num_expert_group must be in [1, 64] and divide E (got %d, E = %d)", fn,
+                num_expert_group, E);
+  if (topk_group < 1 || topk_group > num_expert_group)
+    return fail(MOE_EINVAL, "%s: topk_group must be in [1, num_expert_group] (got %d)", fn, topk_group);
+  if (topk < 1 || topk > 32 || topk > topk_group * (E / num_expert_group))
+    return fail(MOE_EINVAL, "%s: topk must be in [1, min(32, topk_group * E / num_expert_group)] (got %d)", fn, topk);
+  if (n_shared < 0 || n_shared > 32) return fail(MOE_EINVAL, "%s: n_shared must be in [0, 32] (got %d)", fn, n_shared);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return fail(MOE_EINVAL, "%s: unknown score %d", fn, (int)score);
+  if (T > 0 && (!router_logits || !topk_ids || !topk_weights)) return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(router_logits, 4) || !aligned(correction_bias, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+  return hip_status(moe::launch_route_grouped_topk(router_logits, correction_bias, T, E, topk, num_expert_group,
+                                                   topk_group, (int)score, renormalize ? 1 : 0, routed_scaling_factor,
+                                                   n_shared, shared_weight, topk_ids, topk_weights, stream),
+                    "moe_route_grouped_topk launch");
+}
+
 size_t moe_sort_capacity(int T, int K, int E_total, int block_m) {
   if (T < 0 || K < 0 || E_total < 0 || block_m < 1) return 0;
   return (size_t)T * K + (size_t)E_total * (block_m - 1);

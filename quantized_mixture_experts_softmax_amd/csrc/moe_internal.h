@@ -29,7 +29,7 @@ struct GemmParams {
   int num_blocks;      // grid rows: capacity / block_m
   // stage 1 output: h bf16 [cap, I]
   uint16_t* h;
-  // stage 2 output: ybuf fp32 [T*K, H] by slot id, weighted by topk_weights
+  // stage 2 output: ybuf fp32 [T*K, H] by slot id (the combine applies topk_weights)
   float* ybuf;
   const float* topk_weights;
   int strips_per_wg;   // small-block kernel: consecutive column strips one workgroup streams
@@ -38,6 +38,9 @@ struct GemmParams {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
                              float shared_w, int32_t* ids, float* weights, hipStream_t stream);
+hipError_t launch_route_grouped_topk(const float* logits, const float* bias, int T, int E, int topk, int n_group,
+                                     int topk_group, int score, int renorm, float scaling, int n_shared,
+                                     float shared_w, int32_t* ids, float* weights, hipStream_t stream);
 hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, int32_t* counts, int32_t* offsets,
                              int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 // Router + align-sort in a single one-workgroup launch; only when route_sort_fusable(T, E, K)

@@ -125,6 +125,12 @@ def make_logits(w: Workload, T: int | None = None) -> np.ndarray:
     return (logp[None, :] + g).astype(np.float32)
 
 
+def make_correction_bias(w: Workload) -> np.ndarray:
+    """Score-correction bias [E] fp32 for the grouped router: N(0, 0.05^2), drawn from
+    its own generator (seed + 7) so the other draws of the workload are unchanged."""
+    return np.random.default_rng(w.seed + 7).normal(0.0, 0.05, w.E).astype(np.float32)
+
+
 def _expert_codes(seq, shape, fp8: bool) -> np.ndarray:
     """Uniform random bytes for one expert.  FP8: the e4m3 exponent field is held in
     [4, 7], so codes are finite (no NaN) with |value| in [0.125, 1.875] and a random

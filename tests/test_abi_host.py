@@ -50,6 +50,27 @@ def test_route_rejects(lib):
     assert lib.moe_route_topk(P(FAKE), 4, 2048, 2, 0, 1, 0, 1.0, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
 
 
+def test_route_grouped_rejects(lib):
+    P = ctypes.c_void_p
+    f = lambda *a: lib.moe_route_grouped_topk(*a)
+    ok = [P(FAKE), None, 4, 256, 8, 8, 4, 1, 1, 1.0, 0, 1.0, P(FAKE), P(FAKE), None]
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    # (ok itself is valid and would launch: every call below breaks exactly one limit)
+    assert with_(5, 7) == B.MOE_EINVAL       # 7 groups do not divide 256 experts
+    assert "num_expert_group" in B.moe_last_error()
+    assert with_(5, 128) == B.MOE_EINVAL     # more than 64 groups
+    assert with_(6, 9) == B.MOE_EINVAL       # topk_group > groups
+    assert with_(4, 129) == B.MOE_EINVAL     # topk > 32
+    a = list(ok); a[3] = 16; a[5] = 8; a[6] = 1; a[4] = 3
+    assert f(*a) == B.MOE_EINVAL             # 3 slots > 1 kept group x 2 experts
+    assert with_(1, P(FAKE + 2)) == B.MOE_EINVAL  # misaligned bias
+    assert with_(0, None) == B.MOE_EINVAL    # NULL logits with T > 0
+    assert with_(7, 3) == B.MOE_EINVAL       # unknown score
+
+
 def test_sort_rejects(lib):
     P = ctypes.c_void_p
     assert lib.moe_align_sort(P(FAKE), 4, 2, 8, 48, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
