@@ -505,15 +505,35 @@ static double dot(const double* a, const double* b, int n) {
   return acc;
 }
 
-/* SiLU and the gated product ([rocm_aiter_moe] AiterExperts: activation SILU,
- * act-and-mul only): h = silu(gate) * up with silu(z) = z / (1 + e^-z). */
-static double silu_mul(double g, double u) { return g / (1.0 + exp(-g)) * u; }
+/* The gated activation of one output column.
+ * SILU ([rocm_aiter_moe] AiterExperts: activation SILU, act-and-mul only):
+ *   h = silu(gate) * up with silu(z) = z / (1 + e^-z).
+ * SWIGLU_OAI: the pages give only its name ([rocm_aiter_moe] _resolve_aiter_activation,
+ * SWIGLUOAI mapped to the kernel's "swiglu") and its constants ([mxfp4.py]
+ * Mxfp4MoEMethod.get_fused_moe_quant_config: gemm1_alpha 1.702, gemm1_beta 1.0,
+ * swiglu_limit 7.0; rocm_aiter_fused_experts passes limit 0.0 when there is none).
+ * Reading (the published gpt-oss activation these constants belong to): the gate is
+ * clamped from above at the limit, the up value to [-limit, limit] (no clamping when
+ * limit <= 0), and h = gate * sigmoid(alpha * gate) * (up + beta). */
+static double glu(const orc_layer* L, double g, double u) {
+  if (L->act == ORC_ACT_SILU) return g / (1.0 + exp(-g)) * u;
+  if (L->limit > 0.0) {
+    if (g > L->limit) g = L->limit;
+    if (u > L->limit) u = L->limit;
+    if (u < -L->limit) u = -L->limit;
+  }
+  return g / (1.0 + exp(-L->alpha * g)) * (u + L->beta);
+}
+
+/* bf16 bias value, 0 without a bias tensor. */
+static double bias_at(const uint16_t* b, size_t i) { return b ? (double)orc_bf16_to_f32(b[i]) : 0.0; }
 
 static int layer_ok(const orc_layer* L) {
   if (!L || L->H <= 0 || L->I <= 0 || L->E_total <= 0 || L->K <= 0) return 0;
   if (L->H % 32 || L->I % 32) return 0;
   if (L->wfmt < ORC_W_MXFP4 || L->wfmt > ORC_W_FP8_CHANNEL) return 0;
   if (L->afmt < ORC_A_BF16 || L->afmt > ORC_A_FP8_TOKEN) return 0;
+  if (L->act != ORC_ACT_SILU && L->act != ORC_ACT_SWIGLU_OAI) return 0;
   return 1;
 }
 
@@ -525,10 +545,13 @@ int orc_num_threads(void) {
 #endif
 }
 
-/* Stage 1: for slot j of token t routed to expert e, gate_n = <a, W1[e][n]>,
- * up_n = <a, W1[e][I + n]> (w13 holds gate rows then up rows, the SEPARATED
- * gate/up layout of [rocm_aiter_moe] rocm_aiter_fused_experts and
- * [mxfp4.py] Mxfp4MoEMethod._setup_kernel_k3_situ), h_n = bf16(silu(gate_n) * up_n). */
+/* Stage 1: for slot j of token t routed to expert e, gate_n = <a, W1[e][rg]> + b1[e][rg],
+ * up_n = <a, W1[e][ru]> + b1[e][ru], h_n = bf16(act(gate_n, up_n)).  Rows: rg = n,
+ * ru = I + n (gate rows then up rows, the SEPARATED gate/up layout of [rocm_aiter_moe]
+ * rocm_aiter_fused_experts and [mxfp4.py] Mxfp4MoEMethod._setup_kernel_k3_situ), or
+ * rg = 2n, ru = 2n + 1 (the INTERLEAVE gate mode [rocm_aiter_moe]
+ * mxfp4_w4a16_extra_kwargs selects for MXFP4 w4a16).  Biases are bf16 [E, 2I] in the
+ * same row order ([mxfp4.py] Mxfp4MoEMethod.create_weights: w13_bias). */
 int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
                const int32_t* tokens, int n_tok, uint16_t* h) {
   if (!layer_ok(L) || n_tok < 0) return -1;
@@ -559,11 +582,13 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
           continue;
         }
         for (int n = 0; n < I; ++n) {
-          weight_row(L->wfmt, L->w1, L->w1_scale, e, n, 2 * I, H, wr);
-          const double g = dot(a, wr, H);
-          weight_row(L->wfmt, L->w1, L->w1_scale, e, I + n, 2 * I, H, wr);
-          const double u = dot(a, wr, H);
-          hrow[n] = orc_f64_to_bf16(silu_mul(g, u));
+          const int rg = L->gate_up_interleaved ? 2 * n : n;
+          const int ru = L->gate_up_interleaved ? 2 * n + 1 : I + n;
+          weight_row(L->wfmt, L->w1, L->w1_scale, e, rg, 2 * I, H, wr);
+          const double g = dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + rg);
+          weight_row(L->wfmt, L->w1, L->w1_scale, e, ru, 2 * I, H, wr);
+          const double u = dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + ru);
+          hrow[n] = orc_f64_to_bf16(glu(L, g, u));
         }
       }
     }
@@ -573,7 +598,8 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
   return err ? -1 : 0;
 }
 
-/* Stage 2: y_m = <h_slot, W2[e][m]> and out_m = sum over the token's slots, in
+/* Stage 2: y_m = <h_slot, W2[e][m]> + b2[e][m] (bf16 bias [E, H], [mxfp4.py]
+ * Mxfp4MoEMethod.create_weights: w2_bias) and out_m = sum over the token's slots, in
  * ascending slot order, of topk_weight * y_m.  The weights multiply the down
  * projection's output and the reduction belongs to the expert computation itself
  * ([rocm_aiter_moe] AiterExperts.finalize_weight_and_reduce_impl is a no-op;
@@ -608,7 +634,7 @@ int orc_stage2(const orc_layer* L, const uint16_t* h, const int32_t* topk_ids, c
         const double wj = (double)topk_weights[(size_t)t * K + j];
         for (int m = 0; m < H; ++m) {
           weight_row(L->wfmt, L->w2, L->w2_scale, e, m, H, I, wr);
-          orow[m] += wj * dot(a, wr, I);
+          orow[m] += wj * (dot(a, wr, I) + bias_at(L->w2_bias, (size_t)e * H + m));
         }
       }
     }

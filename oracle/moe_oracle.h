@@ -59,15 +59,24 @@ int orc_align_sort(const int32_t* topk_ids, int T, int K, int E_total, int block
 int orc_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes, void* scales);
 
 /* ---- expert layer ---- */
+/* Gated activations. */
+enum { ORC_ACT_SILU = 0, ORC_ACT_SWIGLU_OAI = 1 };
+
 typedef struct {
   int H, I, E_total, K;       /* hidden, intermediate, experts in the weight tensors, slots per token */
   int wfmt, afmt;
   const uint8_t* w1; const void* w1_scale;   /* [E_total][2I][..] */
   const uint8_t* w2; const void* w2_scale;   /* [E_total][H][..]  */
+  int act;                    /* ORC_ACT_SILU or ORC_ACT_SWIGLU_OAI */
+  double alpha, beta, limit;  /* SwiGLU-OAI parameters (limit <= 0: no clamping) */
+  int gate_up_interleaved;    /* 0: w13 rows [gate_0..gate_{I-1}, up_0..up_{I-1}]; 1: gate_n, up_n alternate */
+  const uint16_t* w1_bias;    /* bf16 [E_total][2I] in w13 row order, or NULL */
+  const uint16_t* w2_bias;    /* bf16 [E_total][H], or NULL */
 } orc_layer;
 
 /* Stage 1 for the tokens listed in `tokens` (n_tok of them):
- *   h[(i*K + j)*I + n] = bf16( silu(g) * u ) for slot j of token tokens[i].
+ *   h[(i*K + j)*I + n] = bf16( act(g, u) ) for slot j of token tokens[i], g and u the
+ *   gate and up rows' dot products plus their biases.
  * Activations are x (bf16) or, for quantised formats, x quantised and dequantised
  * per row with the layer's activation format. */
 int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,

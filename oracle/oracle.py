@@ -38,6 +38,13 @@ Which test pins which oracle function (tests/test_oracle_*.py, all CPU):
       fp64 brute force on tiny shapes; token-permutation and expert-relabelling
       invariance; +1 on every w2 E8M0 byte doubles the output; zero weight slot
       contributes nothing.
+  SwiGLU-OAI, biases, interleaved gate/up rows (orc_stage1 / orc_stage2 options)
+      alpha 1, beta 0, no limit equals the SiLU layer bit for bit; interleaved rows
+      (codes, scales, biases permuted with numpy) equal separated rows bit for bit, and
+      the unpermuted rows do not; the down-projection bias adds sum_j w_j * b2[e_j]
+      (numpy einsum); with zero w1 codes (gate and up = biases) the clamp's
+      invariances: gate clamped from above only, up on both sides, none at limit 0,
+      zero at up = -beta or gate = 0, increasing in the gate below the limit.
 """
 from __future__ import annotations
 
@@ -252,7 +259,13 @@ class _Layer(ctypes.Structure):
         ("wfmt", ctypes.c_int), ("afmt", ctypes.c_int),
         ("w1", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
         ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+        ("act", ctypes.c_int), ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("limit", ctypes.c_double),
+        ("gate_up_interleaved", ctypes.c_int),
+        ("w1_bias", ctypes.c_void_p), ("w2_bias", ctypes.c_void_p),
     ]
+
+
+ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
 
 @dataclass
@@ -268,12 +281,23 @@ class Layer:
     w1_scale: np.ndarray
     w2: np.ndarray
     w2_scale: np.ndarray
+    act: int = ACT_SILU
+    alpha: float = 1.702
+    beta: float = 1.0
+    limit: float = 7.0
+    gate_up_interleaved: bool = False
+    w1_bias: np.ndarray | None = None  # bf16 bits [E_total, 2I] in w1 row order
+    w2_bias: np.ndarray | None = None  # bf16 bits [E_total, H]
 
     def _c(self) -> _Layer:
-        for a in (self.w1, self.w1_scale, self.w2, self.w2_scale):
-            assert a.flags["C_CONTIGUOUS"]
+        for a in (self.w1, self.w1_scale, self.w2, self.w2_scale, self.w1_bias, self.w2_bias):
+            assert a is None or a.flags["C_CONTIGUOUS"]
+        for b, n in ((self.w1_bias, 2 * self.I), (self.w2_bias, self.H)):
+            assert b is None or (b.dtype == np.uint16 and b.shape == (self.E_total, n))
         return _Layer(self.H, self.I, self.E_total, self.K, self.wfmt, self.afmt,
-                      _ptr(self.w1), _ptr(self.w1_scale), _ptr(self.w2), _ptr(self.w2_scale))
+                      _ptr(self.w1), _ptr(self.w1_scale), _ptr(self.w2), _ptr(self.w2_scale),
+                      self.act, self.alpha, self.beta, self.limit, int(self.gate_up_interleaved),
+                      _ptr(self.w1_bias), _ptr(self.w2_bias))
 
 
 def _tokens(T: int, tokens) -> np.ndarray:

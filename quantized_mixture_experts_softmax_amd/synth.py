@@ -131,6 +131,22 @@ def make_correction_bias(w: Workload) -> np.ndarray:
     return np.random.default_rng(w.seed + 7).normal(0.0, 0.05, w.E).astype(np.float32)
 
 
+def make_biases(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 biases (bits) of the two projections, [E_total, 2I] and [E_total, H], N(0, 0.1^2),
+    from their own generator (seed + 11) so the other draws are unchanged."""
+    rng = np.random.default_rng(w.seed + 11)
+    b1 = f32_to_bf16_bits(rng.normal(0.0, 0.1, (w.E_total, 2 * w.I)).astype(np.float32))
+    b2 = f32_to_bf16_bits(rng.normal(0.0, 0.1, (w.E_total, w.H)).astype(np.float32))
+    return b1, b2
+
+
+def interleave_rows(a: np.ndarray, I: int) -> np.ndarray:
+    """Reorders axis 1 of a [E, 2I, ...] tensor from [gate_0..gate_{I-1}, up_0..up_{I-1}]
+    to gate_0, up_0, gate_1, up_1, ... (a pure permutation of rows)."""
+    order = np.stack([np.arange(I), I + np.arange(I)], axis=1).reshape(-1)
+    return np.ascontiguousarray(a[:, order])
+
+
 def _expert_codes(seq, shape, fp8: bool) -> np.ndarray:
     """Uniform random bytes for one expert.  FP8: the e4m3 exponent field is held in
     [4, 7], so codes are finite (no NaN) with |value| in [0.125, 1.875] and a random
