@@ -116,15 +116,16 @@ def traffic_from_profiles(workload_name: str):
     return float(vals["TRAFFIC_BYTES_PER_LAUNCH"])
 
 
-def cpu_baseline(w, data, seconds: float):
-    """The oracle, as it stands, on a bounded sample of the same workload (rank 0, N=1)."""
+def cpu_baseline(w, data, seconds: float, act_host: dict | None = None):
+    """The oracle, as it stands, on a bounded sample of the same workload (rank 0, N=1).
+    act_host: SwiGLU-OAI settings and host bias arrays when the layer uses them."""
     import numpy as np
 
     from oracle import oracle as orc
 
     ids, wts = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
     L = orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
-                  data["w2_scale"])
+                  data["w2_scale"], **(act_host or {}))
     per_call = max(1, min(w.T, 64))
     done, t0, start = 0, time.perf_counter(), 0
     while True:
@@ -155,6 +156,9 @@ def main() -> int:
                     help="weight layout: the kernel layout prepared once by moe_tile_weights, or canonical")
     ap.add_argument("--router", choices=["plain", "grouped"], default="plain",
                     help="grouped: group-limited router (8 groups, 4 kept, seeded correction bias, scaling 2.5)")
+    ap.add_argument("--act", choices=["silu", "swiglu-oai"], default="silu",
+                    help="swiglu-oai: SwiGLU-OAI (alpha 1.702, beta 1, limit 7) with interleaved gate/up rows and "
+                         "seeded bf16 biases on both projections (the gpt-oss layer form)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=10,
@@ -194,13 +198,26 @@ def main() -> int:
             return 2
         grouped = dict(num_expert_group=8, topk_group=4, routed_scaling_factor=2.5,
                        correction_bias=t(synth.make_correction_bias(w)))
+    act = act_host = None
+    if args.act == "swiglu-oai":
+        if w.wfmt == synth.W_FP8_BLOCK128:
+            print("bench.py: --act swiglu-oai interleaves w13 rows, which FP8 128x128 block scales do not allow",
+                  file=sys.stderr)
+            return 2
+        b1, b2 = synth.make_biases(w)
+        data = dict(data, w1=synth.interleave_rows(data["w1"], w.I), w1_scale=synth.interleave_rows(data["w1_scale"], w.I))
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+        act = dict(kind=B.ACT_SWIGLU_OAI, alpha=1.702, beta=1.0, limit=7.0, interleaved=True,
+                   w1_bias=bf(synth.interleave_rows(b1, w.I)), w2_bias=bf(b2))
+        act_host = dict(act=1, alpha=1.702, beta=1.0, limit=7.0, gate_up_interleaved=True,
+                        w1_bias=synth.interleave_rows(b1, w.I), w2_bias=b2)
     layers = []
     for _ in range(copies):
         layers.append(B.MoELayer(t(data["w1"]), t(data["w1_scale"]), t(data["w2"]), t(data["w2_scale"]), H=w.H,
                                  I=w.I, E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
                                  score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                                  n_shared=w.n_shared, shared_weight=w.shared_weight, block_m=args.block_m,
-                                 tiled=args.layout == "tiled", grouped=grouped))
+                                 tiled=args.layout == "tiled", grouped=grouped, act=act))
     x = torch.from_numpy(data["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     logits = t(data["logits"])
     hip = _hip()
@@ -276,7 +293,8 @@ def main() -> int:
                    "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
                    "weight_layout": args.layout,
-                   "router_kind": "grouped (8 groups, 4 kept, bias, scaling 2.5)" if grouped else "plain top-k"},
+                   "router_kind": "grouped (8 groups, 4 kept, bias, scaling 2.5)" if grouped else "plain top-k",
+                   "activation": "swiglu-oai, interleaved w13, biases" if act else "silu-and-mul"},
         "roofline": roof,
         "step_breakdown_us": {"gpu_step": round(gpu_ms * 1e3 / args.steps, 2),
                               "stage1_gemm": round(g1_ms * 1e3, 2), "a2_quant+stage2_gemm": round(float(np.mean(g2)) * 1e3, 2),
@@ -293,7 +311,7 @@ def main() -> int:
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds, act_host)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -76,9 +76,17 @@ typedef enum moe_afmt { MOE_A_BF16 = 0, MOE_A_MXFP4_G32 = 1, MOE_A_FP8_G128 = 2,
  *                         process_weights_after_loading); this is that step for this library. */
 typedef enum moe_weight_layout { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED = 1 } moe_weight_layout;
 
-/* Gated activation.  Only SiLU-and-mul: h = silu(gate) * up, silu(z) = z / (1 + e^-z)
- * ([rocm_aiter_moe] AiterExperts: SILU activation, act-and-mul only). */
-typedef enum moe_act { MOE_ACT_SILU = 0 } moe_act;
+/* Gated activation of stage 1 (gate and up are the two w13 rows of an output column,
+ * each plus its bias when w1_bias is given):
+ *   MOE_ACT_SILU        h = silu(gate) * up, silu(z) = z / (1 + e^-z)
+ *                       ([rocm_aiter_moe] AiterExperts: SILU activation, act-and-mul only)
+ *   MOE_ACT_SWIGLU_OAI  gate = min(gate, limit), up = clamp(up, -limit, limit) (no clamping
+ *                       when limit <= 0), h = gate * sigmoid(alpha * gate) * (up + beta).
+ *                       The pages name it (SWIGLUOAI, [rocm_aiter_moe]
+ *                       _resolve_aiter_activation) and give alpha 1.702, beta 1.0, limit 7.0
+ *                       ([mxfp4.py] Mxfp4MoEMethod.get_fused_moe_quant_config); the formula is
+ *                       the published gpt-oss activation those constants belong to. */
+typedef enum moe_act { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
 
 /* ------------------------------------------------------------------------------------
  * moe_route_topk -- softmax / sigmoid top-k router with optional shared-expert slots.
@@ -196,10 +204,11 @@ moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
  *
  * For every slot (t, j) routed to expert e = topk_ids[t, j] (shared experts are ordinary
  * experts with ids >= the routed count, carried as extra slots):
- *   stage 1  [g | u] = a1[t] . w1[e]^T   (g: rows [0, I) of w1, u: rows [I, 2I))
- *            h = bf16( silu(g) * u )      fused into the GEMM epilogue
+ *   stage 1  [g | u] = a1[t] . w1[e]^T (+ w1_bias[e])  (g: rows [0, I) of w1, u: rows
+ *            [I, 2I); with gate_up_interleaved g and u of column n are rows 2n and 2n+1)
+ *            h = bf16( act(g, u) )        fused into the GEMM epilogue (see moe_act)
  *            for quantised activation formats h is re-quantised (a2) in the same format
- *   stage 2  y = a2 . w2[e]^T, scaled by topk_weights[t, j]
+ *   stage 2  y = a2 . w2[e]^T (+ w2_bias[e]), scaled by topk_weights[t, j]
  *   out[t] = bf16( sum over j = 0..K-1, in ascending j, of the weighted y )
  * (the weighted reduction is part of the expert computation: [rocm_aiter_moe]
  * AiterExperts.finalize_weight_and_reduce_impl is a no-op and the weights apply to the
@@ -233,6 +242,14 @@ typedef struct moe_forward_args {
   void* workspace;
   size_t workspace_bytes;
   moe_weight_layout weight_layout;               /* layout of w1 and w2 (both the same) */
+  float act_alpha, act_beta, act_limit;          /* MOE_ACT_SWIGLU_OAI parameters (else unused) */
+  int gate_up_interleaved;                       /* 0: w1 rows [gate_0..gate_{I-1}, up_0..up_{I-1}];
+                                                    1: gate_n, up_n alternate (the INTERLEAVE gate
+                                                    mode of [rocm_aiter_moe]
+                                                    mxfp4_w4a16_extra_kwargs); not for FP8_BLOCK128 */
+  const uint16_t* w1_bias;                       /* bf16 [E_total, 2I] in w1 row order, or NULL */
+  const uint16_t* w2_bias;                       /* bf16 [E_total, H], or NULL ([mxfp4.py]
+                                                    create_weights: w13_bias, w2_bias) */
 } moe_forward_args;
 
 /* Byte offsets into the workspace (each 256-byte aligned); 0 size = not used. */

@@ -18,7 +18,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 SCORE = {"softmax": 0, "sigmoid": 1}
 W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
 A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
-ACT_SILU = 0
+ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
 EXPORTED = [
     "moe_route_topk", "moe_route_grouped_topk", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
@@ -49,6 +49,9 @@ class ForwardArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("weight_layout", ctypes.c_int),
+        ("act_alpha", ctypes.c_float), ("act_beta", ctypes.c_float), ("act_limit", ctypes.c_float),
+        ("gate_up_interleaved", ctypes.c_int),
+        ("w1_bias", ctypes.c_void_p), ("w2_bias", ctypes.c_void_p),
     ]
 
 
@@ -276,12 +279,23 @@ def moe_quant_act(x: torch.Tensor, fmt: int, codes=None, scales=None, stream=Non
 
 def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
                  afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
-                 a1_scales=None, weight_layout: int = LAYOUT_CANONICAL) -> ForwardArgs:
+                 a1_scales=None, weight_layout: int = LAYOUT_CANONICAL, act: dict | None = None) -> ForwardArgs:
+    """act: None (SiLU-and-mul) or dict(kind=ACT_SILU | ACT_SWIGLU_OAI, alpha, beta, limit,
+    interleaved, w1_bias, w2_bias) -- biases are bf16 tensors [E, 2I] / [E, H] or None."""
     T, H = hidden_states.shape
     K = topk_ids.shape[1]
     a = ForwardArgs()
     a.T, a.H, a.I, a.E_total, a.K, a.block_m = T, H, I, E_total, K, block_m
-    a.wfmt, a.afmt, a.act = wfmt, afmt, ACT_SILU
+    act = act or {}
+    a.wfmt, a.afmt, a.act = wfmt, afmt, act.get("kind", ACT_SILU)
+    a.act_alpha, a.act_beta, a.act_limit = act.get("alpha", 1.702), act.get("beta", 1.0), act.get("limit", 7.0)
+    a.gate_up_interleaved = int(bool(act.get("interleaved", False)))
+    for name, n in (("w1_bias", 2 * I), ("w2_bias", H)):
+        b = act.get(name)
+        if b is not None:
+            assert b.dtype == torch.bfloat16 and b.shape == (E_total, n), (name, b.shape)
+            _dev(b)
+        setattr(a, name, _ptr(b))
     a.hidden_states = _ptr(hidden_states)
     a.a1_codes, a.a1_scales = _ptr(a1_codes), _ptr(a1_scales)
     a.w1, a.w1_scale, a.w2, a.w2_scale = _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale)
@@ -310,15 +324,16 @@ def moe_workspace_layout(args: ForwardArgs) -> dict:
 
 def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict, wfmt: int,
                         afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
-                        a1_scales=None, stream=None, weight_layout: int = LAYOUT_CANONICAL):
-    """Returns (out, workspace).  The workspace may be passed back in on later calls."""
+                        a1_scales=None, stream=None, weight_layout: int = LAYOUT_CANONICAL, act: dict | None = None):
+    """Returns (out, workspace).  The workspace may be passed back in on later calls.
+    act: see forward_args."""
     dev = _dev(hidden_states)
     assert hidden_states.dtype == torch.bfloat16
     T, H = hidden_states.shape
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     args = forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort, wfmt, afmt,
-                        block_m, E_total, I, out, workspace, a1_codes, a1_scales, weight_layout)
+                        block_m, E_total, I, out, workspace, a1_codes, a1_scales, weight_layout, act)
     need = moe_experts_workspace_bytes(args)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -335,10 +350,11 @@ class MoELayer:
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
-                 tiled: bool = False, grouped: dict | None = None):
+                 tiled: bool = False, grouped: dict | None = None, act: dict | None = None):
         """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights).
         grouped = dict(num_expert_group, topk_group, correction_bias (tensor or None),
-        routed_scaling_factor) routes with moe_route_grouped_topk (then moe_align_sort)."""
+        routed_scaling_factor) routes with moe_route_grouped_topk (then moe_align_sort).
+        act: activation, row order and biases, as for forward_args (None: SiLU-and-mul)."""
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
             w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
@@ -353,6 +369,7 @@ class MoELayer:
         self.K = topk + n_shared
         self.block_m = block_m
         self.grouped = grouped
+        self.act = act
         self._bufs: dict = {}
 
     def _buffers(self, T: int, dev):
@@ -396,5 +413,5 @@ class MoELayer:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
         out, b["workspace"] = moe_experts_forward(
             x, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"], self.wfmt, self.afmt,
-            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout)
+            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
         return out

@@ -126,7 +126,16 @@ struct WLayout {
   }
 };
 
-template <int STAGE, int WF, int AF, int BM, int NT, int WL>
+// EPI (all GEMM kernels): 0 = SiLU-and-mul, separated gate/up rows, no bias, compiled
+// without the branches of the general epilogue (its registers and code size matter on
+// the hot path); 1 = activation, row order and biases as GemmParams says.
+template <int EPI>
+__device__ __forceinline__ float glu(const GemmParams& p, float g, float u) {
+  if constexpr (EPI == 0) return g / (1.0f + __expf(-g)) * u;
+  else return glu_act(p, g, u);
+}
+
+template <int STAGE, int WF, int AF, int BM, int NT, int WL, int EPI>
 // 64-row blocks: the register budget keeps two waves per SIMD resident (measured: up to
 // 1.8x faster than one); 128-row blocks would spill under that budget.
 __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const GemmParams p) {
@@ -205,22 +214,33 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   const uint8_t* ws_src[NT];
   const float* wsb_src[NT];
   float wsc[NT];
-  int col[NT];
+  int col[NT], wrow[NT];
   bool col_ok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int c, trow;
     if (STAGE == 1) {
-      const int tt = t % (NT / 2);
-      c = nt_idx * COLS_PER_WG + w * (NT / 2) * 16 + tt * 16 + li;
-      col_ok[t] = c < p.N;
-      trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
+      // the wave's output columns [cb, cb + 8 NT): separated rows pair gate tile t with
+      // up tile t + NT/2; interleaved rows are tiles [2 cb + 16 t, +16), gate and up of
+      // columns cb + 8 t + (0..7) in alternate lanes
+      const int cb = nt_idx * COLS_PER_WG + w * (NT / 2) * 16;
+      if ((EPI && p.interleaved)) {
+        c = cb + 8 * t + (li >> 1);
+        col_ok[t] = 2 * cb + 16 * t < p.Nw;
+        trow = col_ok[t] ? 2 * cb + 16 * t : 0;
+      } else {
+        const int tt = t % (NT / 2);
+        c = cb + tt * 16 + li;
+        col_ok[t] = c < p.N;
+        trow = col_ok[t] ? (t < NT / 2 ? c - li : p.N + c - li) : 0;
+      }
     } else {
       c = nt_idx * COLS_PER_WG + w * NT * 16 + t * 16 + li;
       col_ok[t] = c < p.N;
       trow = col_ok[t] ? c - li : 0;
     }
     col[t] = c;
+    wrow[t] = trow + li;
     w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
     ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
     wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
@@ -420,25 +440,47 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
 
   // ---- epilogue ----
   if constexpr (STAGE == 1) {
+    float bsv[NT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int t = 0; t < NT; ++t) bsv[t] = (EPI && p.bias && col_ok[t]) ? bias_of(p, e, wrow[t]) : 0.0f;
+    if ((EPI && p.interleaved)) {
 #pragma unroll
-      for (int t = 0; t < NT / 2; ++t) {
-        if (!col_ok[t]) continue;
-        const int tu = t + NT / 2;
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = m * 16 + 4 * g + rr;
-          float gv = acc[m][t][rr], uv = acc[m][tu][rr];
-          if (WF == kWFp8Channel) {
-            const float as = lds_as[0][row];
-            gv = gv * as * wsc[t];
-            uv = uv * as * wsc[tu];
+        for (int t = 0; t < NT; ++t) {
+          if (!col_ok[t]) continue;  // wave-uniform: tiles never straddle the edge
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = m * 16 + 4 * g + rr;
+            float v = acc[m][t][rr];
+            if (WF == kWFp8Channel) v = v * lds_as[0][row] * wsc[t];
+            v += bsv[t];
+            const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
+            if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
           }
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
-          p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(hv);
         }
-      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT / 2; ++t) {
+          if (!col_ok[t]) continue;
+          const int tu = t + NT / 2;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = m * 16 + 4 * g + rr;
+            float gv = acc[m][t][rr], uv = acc[m][tu][rr];
+            if (WF == kWFp8Channel) {
+              const float as = lds_as[0][row];
+              gv = gv * as * wsc[t];
+              uv = uv * as * wsc[tu];
+            }
+            gv += bsv[t];
+            uv += bsv[tu];
+            p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+          }
+        }
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -453,6 +495,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
           if (!col_ok[t]) continue;
           float v = acc[m][t][rr];
           if (WF == kWFp8Channel) v = v * as * wsc[t];
+          if (EPI && p.bias) v += bias_of(p, e, col[t]);
           p.ybuf[(size_t)slot * p.N + col[t]] = v;
         }
       }
@@ -480,7 +523,7 @@ struct ARegs {
   float as[MT][4];                                          // FP8 block: scales of the 4 output rows
 };
 
-template <int STAGE, int WF, int AF, int BM, int NT, int WL>
+template <int STAGE, int WF, int AF, int BM, int NT, int WL, int EPI>
 __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int MT = BM / 16;
@@ -510,14 +553,24 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
   const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
   const int nbn = (p.Nw + 127) / 128, nbk = nch;
 
-  // weight row of tile t in strip s for this lane (lane li = column inside the tile)
+  // Output column of this lane for tile t of strip s (stage 1 interleaved rows: the
+  // columns of a tile are cb + 8 t + li / 2, gate in even lanes, up in odd ones), and
+  // the first weight row of the lane's tile (0 for tiles past the edge).
   auto tile_col = [&](int s, int t) {
-    return (STAGE == 1) ? (s0 + s) * COLS_PER_STRIP + (t % (NT / 2)) * 16 + li
-                        : (s0 + s) * COLS_PER_STRIP + t * 16 + li;
+    const int cb = (s0 + s) * COLS_PER_STRIP;
+    if (STAGE == 1 && (EPI && p.interleaved)) return cb + 8 * t + (li >> 1);
+    return (STAGE == 1) ? cb + (t % (NT / 2)) * 16 + li : cb + t * 16 + li;
   };
-  auto tile_row = [&](int s, int t) {  // first weight row of the lane's tile (0 for tiles past N)
+  auto tile_ok = [&](int s, int t) {  // wave-uniform
+    const int cb = (s0 + s) * COLS_PER_STRIP;
+    if (STAGE == 1 && (EPI && p.interleaved)) return 2 * cb + 16 * t < p.Nw;
+    return tile_col(s, t) - li < p.N;
+  };
+  auto tile_row = [&](int s, int t) {
+    if (!tile_ok(s, t)) return 0;
+    const int cb = (s0 + s) * COLS_PER_STRIP;
+    if (STAGE == 1 && (EPI && p.interleaved)) return 2 * cb + 16 * t;
     const int c = tile_col(s, t) - li;
-    if (c >= p.N) return 0;
     return (STAGE == 1 && t >= NT / 2) ? p.N + c : c;
   };
 
@@ -676,27 +729,51 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
             acc[m][t][rr] = ((acc[m][t][rr] + red[buf][0][i][lane]) + red[buf][1][i][lane]) + red[buf][2][i][lane];
           }
       if constexpr (STAGE == 1) {
+        if ((EPI && p.interleaved)) {
 #pragma unroll
-        for (int t = 0; t < NT / 2; ++t) {
-          const int col = tile_col(s, t);
-          if (col >= p.N) continue;
-          const int tu = t + NT / 2;
-          const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
-          const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
+          for (int t = 0; t < NT; ++t) {
+            if (!tile_ok(s, t)) continue;
+            const int col = tile_col(s, t), wr = tile_row(s, t) + li;
+            const float ws = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + wr] : 1.0f;
+            const float bs = (EPI && p.bias) ? bias_of(p, e, wr) : 0.0f;
 #pragma unroll
-          for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int row = m * 16 + 4 * g + rr;
-              float gv = acc[m][t][rr], uv = acc[m][tu][rr];
-              if constexpr (WF == kWFp8Channel) {
-                const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f;
-                gv = gv * as * wg;
-                uv = uv * as * wu;
+              for (int rr = 0; rr < 4; ++rr) {
+                const int row = m * 16 + 4 * g + rr;
+                float v = acc[m][t][rr];
+                if constexpr (WF == kWFp8Channel)
+                  v = v * (o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f) * ws;
+                v += bs;
+                const float up = __shfl_xor(v, 1, kWave);
+                if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
               }
-              const float hv = gv / (1.0f + __expf(-gv)) * uv;
-              p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(hv);
-            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT / 2; ++t) {
+            const int col = tile_col(s, t);
+            if (col >= p.N) continue;
+            const int tu = t + NT / 2;
+            const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
+            const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
+            const float bg = (EPI && p.bias) ? bias_of(p, e, col) : 0.0f, bu = (EPI && p.bias) ? bias_of(p, e, p.N + col) : 0.0f;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int row = m * 16 + 4 * g + rr;
+                float gv = acc[m][t][rr], uv = acc[m][tu][rr];
+                if constexpr (WF == kWFp8Channel) {
+                  const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f;
+                  gv = gv * as * wg;
+                  uv = uv * as * wu;
+                }
+                gv += bg;
+                uv += bu;
+                p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+              }
+          }
         }
       } else {
 #pragma unroll
@@ -713,6 +790,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
               if (col >= p.N) continue;
               float v = acc[m][t][rr];
               if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
+              if (EPI && p.bias) v += bias_of(p, e, col);
               p.ybuf[(size_t)slot * p.N + col] = v;
             }
           }
@@ -813,7 +891,7 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
 // tile is XOR-swizzled: 16-byte unit u of row r sits at unit u ^ (r mod units per
 // chunk), so the fragment reads of the 16 rows spread over the LDS banks although each
 // direct load writes 1 KB contiguously.
-template <int STAGE, int WF, int AF, int D, int WAVES, int WL>
+template <int STAGE, int WF, int AF, int D, int WAVES, int WL, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int BM = 16, NT = 2;
@@ -863,8 +941,14 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     const int s0 = (int)((long)S * wv / WAVES), s1 = (int)((long)S * (wv + 1) / WAVES);
     const int n = s1 - s0;          // this wave's steps (may be 0)
 
-    // weight tile t of unit u (relative to ua): first weight row, and whether it exists
-    auto trow_of = [&](int u, int t) { return STAGE == 1 ? (t == 0 ? 16 * (ua + u) : p.N + 16 * (ua + u)) : 32 * (ua + u) + 16 * t; };
+    // weight tile t of unit u (relative to ua): first weight row, and whether it exists.
+    // Stage 1 separated rows: gate tile 16 u and up tile N + 16 u; interleaved rows: the
+    // consecutive tiles 32 u and 32 u + 16 (gate and up of columns 16 u .. 16 u + 15 in
+    // alternate lanes).
+    auto trow_of = [&](int u, int t) {
+      if (STAGE == 1) return (EPI && p.interleaved) ? 32 * (ua + u) + 16 * t : (t == 0 ? 16 * (ua + u) : p.N + 16 * (ua + u));
+      return 32 * (ua + u) + 16 * t;
+    };
     auto tok_of = [&](int u, int t) { return STAGE == 1 ? true : 32 * (ua + u) + 16 * t < p.N; };
 
     // load cursor (unit, chunk) of the next step to fetch
@@ -1025,18 +1109,39 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     // Writes unit u's outputs from a complete sum.
     auto emit = [&](int u) {
       if constexpr (STAGE == 1) {
-        const int col = 16 * (ua + u) + li;
+        // (bias loads and their uses stay inside `if (EPI && p.bias)`: a load whose wait could be
+        // hoisted here would drain the weight ring of the no-bias path)
+        if ((EPI && p.interleaved)) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = 4 * g + rr;
-          float gv = acc[0][rr], uv = acc[1][rr];
-          if constexpr (WF == kWFp8Channel) {
-            const float as = ((const float*)lds_sc)[row];
-            gv = gv * as * csc[0];
-            uv = uv * as * csc[1];
+          for (int t = 0; t < NT; ++t) {
+            const int col = 16 * (ua + u) + 8 * t + (li >> 1);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int row = 4 * g + rr;
+              float v = acc[t][rr];
+              if constexpr (WF == kWFp8Channel) v = v * ((const float*)lds_sc)[row] * csc[t];
+              if (EPI && p.bias) v += bias_of(p, e, trow_of(u, t) + li);
+              const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
+              if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
+            }
           }
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
-          p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(hv);
+        } else {
+          const int col = 16 * (ua + u) + li;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * g + rr;
+            float gv = acc[0][rr], uv = acc[1][rr];
+            if constexpr (WF == kWFp8Channel) {
+              const float as = ((const float*)lds_sc)[row];
+              gv = gv * as * csc[0];
+              uv = uv * as * csc[1];
+            }
+            if (EPI && p.bias) {
+              gv += bias_of(p, e, trow_of(u, 0) + li);
+              uv += bias_of(p, e, trow_of(u, 1) + li);
+            }
+            p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+          }
         }
       } else {
 #pragma unroll
@@ -1051,6 +1156,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
             if (col >= p.N) continue;
             float v = acc[t][rr];
             if constexpr (WF == kWFp8Channel) v = v * as * csc[t];
+            if (EPI && p.bias) v += bias_of(p, e, col);
             p.ybuf[(size_t)slot * p.N + col] = v;
           }
         }
@@ -1179,12 +1285,12 @@ static size_t persist_lds_bytes(int afmt, int K, int waves) {
   return tile16_lds_bytes(afmt, K) + (size_t)waves * 2 * 4 * 64 * 4;
 }
 
-template <int STAGE, int WF, int AF, int WL>
+template <int STAGE, int WF, int AF, int WL, int EPI>
 static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t stream) {
   constexpr int WAVES = MOE_PERSIST_WAVES;
   constexpr int D = (WF == kWMxfp4) ? MOE_PERSIST_DEPTH_F4 : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
   if (p.num_blocks == 0) return hipSuccess;
-  auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL>;
+  auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPersistLdsMax);
@@ -1202,11 +1308,11 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
   return hipGetLastError();
 }
 
-template <int STAGE, int WF, int AF, int BM, int WL>
+template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
     const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
-    if (lds <= kPersistLdsMax) return launch_persist<STAGE, WF, AF, WL>(p_in, lds, stream);
+    if (lds <= kPersistLdsMax) return launch_persist<STAGE, WF, AF, WL, EPI>(p_in, lds, stream);
   }
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;
@@ -1226,26 +1332,31 @@ static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if (G == 0) return hipSuccess;
   if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
   if constexpr (kSplit)
-    moe_gemm_ksplit_kernel<STAGE, WF, AF, BM, NT, WL><<<(unsigned)G, 256, 0, stream>>>(p);
+    moe_gemm_ksplit_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
   else
-    moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL><<<(unsigned)G, 256, 0, stream>>>(p);
+    moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int STAGE, int WF, int AF, int WL>
+template <int STAGE, int WF, int AF, int WL, int EPI>
 static hipError_t launch_bm_wl(int bm, const GemmParams& p, hipStream_t stream) {
   switch (bm) {
-    case 16: return launch_one<STAGE, WF, AF, 16, WL>(p, stream);
-    case 32: return launch_one<STAGE, WF, AF, 32, WL>(p, stream);
-    case 64: return launch_one<STAGE, WF, AF, 64, WL>(p, stream);
-    case 128: return launch_one<STAGE, WF, AF, 128, WL>(p, stream);
+    case 16: return launch_one<STAGE, WF, AF, 16, WL, EPI>(p, stream);
+    case 32: return launch_one<STAGE, WF, AF, 32, WL, EPI>(p, stream);
+    case 64: return launch_one<STAGE, WF, AF, 64, WL, EPI>(p, stream);
+    case 128: return launch_one<STAGE, WF, AF, 128, WL, EPI>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int STAGE, int WF, int AF>
 static hipError_t launch_bm(int bm, const GemmParams& p, hipStream_t stream) {
-  return p.weight_layout ? launch_bm_wl<STAGE, WF, AF, 1>(bm, p, stream) : launch_bm_wl<STAGE, WF, AF, 0>(bm, p, stream);
+  const bool general = p.bias || (STAGE == 1 && (p.act != kActSilu || p.interleaved));
+  if (general)
+    return p.weight_layout ? launch_bm_wl<STAGE, WF, AF, 1, 1>(bm, p, stream)
+                           : launch_bm_wl<STAGE, WF, AF, 0, 1>(bm, p, stream);
+  return p.weight_layout ? launch_bm_wl<STAGE, WF, AF, 1, 0>(bm, p, stream)
+                         : launch_bm_wl<STAGE, WF, AF, 0, 0>(bm, p, stream);
 }
 
 template <int STAGE>

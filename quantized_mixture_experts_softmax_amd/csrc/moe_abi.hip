@@ -69,7 +69,12 @@ moe_status check_shapes(const moe_forward_args* a) {
   if (!valid_bm(a->block_m)) return fail(MOE_EINVAL, "block_m must be 16, 32, 64 or 128 (got %d)", a->block_m);
   if ((long long)a->T * a->K + (long long)a->E_total * a->block_m >= 0x7FFFFFFFLL)
     return fail(MOE_EINVAL, "T*K too large");
-  if (a->act != MOE_ACT_SILU) return fail(MOE_EUNSUPPORTED, "only the SiLU-and-mul activation is implemented");
+  if (a->act != MOE_ACT_SILU && a->act != MOE_ACT_SWIGLU_OAI)
+    return fail(MOE_EUNSUPPORTED, "activation %d is not implemented (SiLU-and-mul, SwiGLU-OAI)", (int)a->act);
+  if (a->gate_up_interleaved != 0 && a->gate_up_interleaved != 1)
+    return fail(MOE_EINVAL, "gate_up_interleaved must be 0 or 1 (got %d)", a->gate_up_interleaved);
+  if (a->gate_up_interleaved && a->wfmt == MOE_W_FP8_BLOCK128)
+    return fail(MOE_EUNSUPPORTED, "interleaved gate/up rows would split FP8 128x128 scale blocks");
   if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
   if (a->afmt < MOE_A_BF16 || a->afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)a->afmt);
   if (!pair_supported(a->wfmt, a->afmt))
@@ -116,7 +121,8 @@ moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w
 }
 
 moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I) {
-  if (act != MOE_ACT_SILU) return fail(MOE_EUNSUPPORTED, "only the SiLU-and-mul activation is implemented");
+  if (act != MOE_ACT_SILU && act != MOE_ACT_SWIGLU_OAI)
+    return fail(MOE_EUNSUPPORTED, "activation %d is not implemented (SiLU-and-mul, SwiGLU-OAI)", (int)act);
   if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
   if (afmt < MOE_A_BF16 || afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)afmt);
   if (!pair_supported(wfmt, afmt))
@@ -283,8 +289,9 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   if (!aligned(a->hidden_states, 16) || !aligned(a->w1, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
       !aligned(a->topk_weights, 4) || !aligned(a->w1_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) ||
       !aligned(a->w2_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) || (a->a1_codes && !aligned(a->a1_codes, 16)) ||
-      (a->a1_scales && !aligned(a->a1_scales, 4)))
-    return fail(MOE_EINVAL, "moe_experts_forward: misaligned pointer (16 B for tensors, 4 B for fp32 arrays)");
+      (a->a1_scales && !aligned(a->a1_scales, 4)) || !aligned(a->w1_bias, 2) || !aligned(a->w2_bias, 2))
+    return fail(MOE_EINVAL, "moe_experts_forward: misaligned pointer (16 B for tensors, 4 B for fp32 arrays, "
+                            "2 B for biases)");
   if (a->afmt != MOE_A_BF16 && (a->a1_codes == nullptr) != (a->a1_scales == nullptr))
     return fail(MOE_EINVAL, "moe_experts_forward: a1_codes and a1_scales go together");
   if (!a->workspace || a->workspace_bytes < L.total)
@@ -320,6 +327,10 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.num_blocks = (int)(cap / a->block_m);
   p.topk_weights = a->topk_weights;
   p.weight_layout = (int)a->weight_layout;
+  p.act = a->act == MOE_ACT_SWIGLU_OAI ? moe::kActSwigluOai : moe::kActSilu;
+  p.act_alpha = a->act_alpha;
+  p.act_beta = a->act_beta;
+  p.act_limit = a->act_limit;
 
   // stage 1: gate/up GEMM + SiLU-and-mul -> h (bf16, sorted rows)
   p.a = a1;
@@ -331,6 +342,8 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.K = a->H;
   p.Nw = 2 * a->I;
   p.h = h;
+  p.interleaved = a->gate_up_interleaved;
+  p.bias = a->w1_bias;
   if ((e = prof_mark(0, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
   e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
@@ -359,6 +372,8 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.Nw = a->H;
   p.h = nullptr;
   p.ybuf = ybuf;
+  p.interleaved = 0;
+  p.bias = a->w2_bias;
   e = moe::launch_gemm(2, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 2");
   if ((e = prof_mark(2, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");

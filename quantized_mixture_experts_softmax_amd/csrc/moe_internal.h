@@ -34,7 +34,32 @@ struct GemmParams {
   const float* topk_weights;
   int strips_per_wg;   // small-block kernel: consecutive column strips one workgroup streams
   int weight_layout;   // 0 canonical, 1 tiled (moe_tile_weights)
+  // Stage 1: gated activation and the order of w13's rows; both stages: optional bf16
+  // bias [E, Nw] indexed by weight row.
+  int act;             // kActSilu or kActSwigluOai
+  float act_alpha, act_beta, act_limit;
+  int interleaved;     // stage 1: w13 rows alternate gate_n, up_n (else gate rows, then up rows)
+  const uint16_t* bias;
 };
+
+constexpr int kActSilu = 0, kActSwigluOai = 1;
+
+// h = act(gate, up) of one output column (stage-1 epilogue).  SiLU: silu(g) * u.
+// SwiGLU-OAI: gate clamped from above at the limit, up to [-limit, limit] (no clamp
+// for limit <= 0), h = g * sigmoid(alpha * g) * (u + beta).
+__device__ __forceinline__ float glu_act(const GemmParams& p, float g, float u) {
+  if (p.act == kActSilu) return g / (1.0f + __expf(-g)) * u;
+  if (p.act_limit > 0.0f) {
+    g = fminf(g, p.act_limit);
+    u = fminf(fmaxf(u, -p.act_limit), p.act_limit);
+  }
+  return g / (1.0f + __expf(-p.act_alpha * g)) * (u + p.act_beta);
+}
+
+// bf16 bias of weight row `row` of expert e (0 without a bias tensor).
+__device__ __forceinline__ float bias_of(const GemmParams& p, int e, int row) {
+  return p.bias ? __uint_as_float((uint32_t)p.bias[(size_t)e * p.Nw + row] << 16) : 0.0f;
+}
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
                              float shared_w, int32_t* ids, float* weights, hipStream_t stream);

@@ -39,9 +39,25 @@ def bf16_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def layer_for(w: synth.Workload, data: dict) -> orc.Layer:
+def layer_for(w: synth.Workload, data: dict, act: dict | None = None) -> orc.Layer:
+    """act (host spec): dict(kind, alpha, beta, limit, interleaved, w1_bias, w2_bias), the
+    biases as bf16 bit arrays or None; data's w1 rows are in the spec's order."""
+    a = act or {}
     return orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
-                     data["w2_scale"])
+                     data["w2_scale"], act=a.get("kind", 0), alpha=a.get("alpha", 1.702), beta=a.get("beta", 1.0),
+                     limit=a.get("limit", 7.0), gate_up_interleaved=bool(a.get("interleaved", False)),
+                     w1_bias=a.get("w1_bias"), w2_bias=a.get("w2_bias"))
+
+
+def act_dev(act: dict | None) -> dict | None:
+    """The host act spec with its biases moved to the GPU as bf16 tensors."""
+    if act is None:
+        return None
+    d = dict(act)
+    for k in ("w1_bias", "w2_bias"):
+        if d.get(k) is not None:
+            d[k] = to_dev(d[k], torch.bfloat16)
+    return d
 
 
 def dev_weights(data: dict) -> dict:
@@ -90,7 +106,8 @@ def check_output(got, ref: np.ndarray, what: str, max_rel=MAX_ABS_REL_RMS, row_l
     return max_rel_err, float(rows.max())
 
 
-def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dict | None = None, tiled=False):
+def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dict | None = None, tiled=False,
+              act: dict | None = None):
     """Route, sort, quantise and run the expert layer on the GPU through the ABI.
     Returns a dict of host copies of every intermediate."""
     wd = wd or dev_weights(data)
@@ -98,7 +115,7 @@ def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dic
     logits = to_dev(data["logits"])
     layer = B.MoELayer(wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], H=w.H, I=w.I, E=w.E, topk=w.topk,
                        wfmt=w.wfmt, afmt=w.afmt, score=score_name(w), n_shared=w.n_shared,
-                       shared_weight=w.shared_weight, block_m=block_m, tiled=tiled)
+                       shared_weight=w.shared_weight, block_m=block_m, tiled=tiled, act=act_dev(act))
     out = layer(x, logits)
     torch.cuda.synchronize()
     b = layer._bufs[(x.shape[0], str(x.device))]

@@ -63,14 +63,14 @@ def check_h_rows(h_gpu, ref_h, what):
     assert rows.max() <= 1e-2
 
 
-def full_check(w, data, res, tokens=None, what=""):
+def full_check(w, data, res, tokens=None, what="", act=None):
     """Parity of one GPU run against the oracle on the listed tokens.
     bf16 activations: the end-to-end output meets the output bound.
     Quantised activations: a2 codes are bit-exact given the GPU's h, the output meets
     the bound against the oracle's stage 2 fed the GPU's h, and the end-to-end result
     (where a2 codes may differ because h was rounded differently) is reported with
     the number of a2 codes that differ, which must stay a small fraction."""
-    L = layer_for(w, data)
+    L = layer_for(w, data, act)
     ids, wts = res["ids"], res["weights"]
     ref_ids, ref_w = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
     assert np.array_equal(ids, ref_ids), f"{what}: topk_ids"
@@ -92,8 +92,10 @@ def full_check(w, data, res, tokens=None, what=""):
     c_ref, _ = orc.quant_act(ref_h[valid], w.afmt)
     c_gpu, _ = orc.quant_act(h_gpu[valid], w.afmt)
     flips = int(np.count_nonzero(c_ref != c_gpu))
+    # one e4m3 code flip moves a row by about 0.125 / sqrt(I) (0.7% at I = 288): the end-to-end
+    # row bound allows for the few flips; the strict bound is the stage-2 check above
     e2e = check_output(acc, ref, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)",
-                       max_rel=0.1, row_l2=1e-2)
+                       max_rel=0.1, row_l2=2e-2)
     assert flips <= max(4, c_ref.size // 500), f"{what}: {flips} a2 code bytes differ"
     return e2e
 
@@ -136,6 +138,60 @@ def test_tile_weights_layout(wfmt, N, K):
     got = B.moe_tile_weights(to_dev(w), to_dev(ws) if ws is not None else None, wfmt, K)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), tiled_reference(wfmt, w, ws, K))
+
+
+def oai_case(w, data, interleaved, bias, kind=1):
+    """Host act spec and matching data: SwiGLU-OAI (alpha 1.702, beta 1, limit 7) or SiLU,
+    optionally interleaved gate/up rows (codes and scales permuted) and biases."""
+    act = dict(kind=kind, alpha=1.702, beta=1.0, limit=7.0, interleaved=interleaved)
+    b1, b2 = synth.make_biases(w) if bias else (None, None)
+    if interleaved:
+        data = dict(data, w1=synth.interleave_rows(data["w1"], w.I),
+                    w1_scale=synth.interleave_rows(data["w1_scale"], w.I))
+        b1 = synth.interleave_rows(b1, w.I) if b1 is not None else None
+    act.update(w1_bias=b1, w2_bias=b2)
+    return act, data
+
+
+OAI = []
+for fmt in (W4A16, W4A4, FP8C):
+    for bm in (16, 32, 64, 128):
+        OAI.append((fmt, bm, True, True, 1))
+for bm in (16, 32, 64, 128):
+    OAI.append((FP8B, bm, False, True, 1))
+OAI += [(W4A16, 16, False, True, 0), (W4A16, 64, False, True, 0), (W4A16, 16, True, False, 1),
+        (W4A16, 64, False, False, 1)]
+
+
+@pytest.mark.parametrize("fmt,bm,itl,bias,kind", OAI,
+                         ids=[f"w{f[0]}a{f[1]}-bm{bm}-{'itl' if i else 'sep'}-{'bias' if b else 'nobias'}-"
+                              f"{'oai' if k else 'silu'}" for f, bm, i, b, k in OAI])
+def test_swiglu_oai_bias_interleave(fmt, bm, itl, bias, kind):
+    """SwiGLU-OAI / SiLU with projection biases and interleaved or separated gate/up rows,
+    every kernel (16/32-row and 64/128-row blocks), against the oracle."""
+    if fmt == FP8B:
+        w = small(fmt, T=40, H=352, I=288, E=5, k=3, n_shared=1, score=synth.SCORE_SIGMOID)
+    elif fmt == FP8C:
+        w = small(fmt, T=33, H=320, I=416, E=4, k=2)
+    else:
+        w = small(fmt)
+    data = synth.make_all(w)
+    act, data = oai_case(w, data, itl, bias, kind)
+    what = f"{w.name}/bm{bm}/{'itl' if itl else 'sep'}/{'bias' if bias else 'nobias'}/{'oai' if kind else 'silu'}"
+    say(f"act forward {what}")
+    res = run_layer(w, data, block_m=bm, tiled=True, act=act)
+    full_check(w, data, res, what=what, act=act)
+
+
+def test_swiglu_oai_decode_full_size():
+    """The decode-shaped layer (H=I=2880, 32 experts, top-4) as a gpt-oss-style layer:
+    SwiGLU-OAI, interleaved w13 rows, both biases, tiled weights, the benchmark's launch
+    configuration; all 64 tokens checked."""
+    w = synth.WORKLOADS["decode"]
+    data = synth.make_all(w)
+    act, data = oai_case(w, data, True, True)
+    res = run_layer(w, data, tiled=True, act=act)
+    full_check(w, data, res, what="decode/oai", act=act)
 
 
 def test_determinism_and_token_permutation():
