@@ -311,6 +311,30 @@ int orc_route_grouped_topk(const float* logits, const float* bias, int T, int E,
   return 0;
 }
 
+/* Expert-parallel share of the layer on one device.  The pages hand an expert map
+ * to the fused kernel as its expert mask ([rocm_aiter_moe] AiterExperts.apply:
+ * expert_mask=expert_map) together with the per-rank count of valid tokens
+ * (num_local_tokens = expert_tokens_meta.expert_num_tokens).  Reading: expert_map
+ * [E_global] holds each global expert's local id on this device, or -1 when it lives
+ * elsewhere; topk_ids keep global ids; token rows at or past num_local_tokens are not
+ * valid here.  The local id of slot (t, j) is expert_map[topk_ids[t, j]] for a valid
+ * row and an id in [0, E_global), else -1 (skipped by the sort and the combine, so the
+ * layer's output is this device's partial sum).  expert_map NULL: identity;
+ * num_local_tokens < 0: every row valid. */
+int orc_map_experts(const int32_t* topk_ids, const int32_t* expert_map, int num_local_tokens, int T, int K,
+                    int E_global, int32_t* local_ids) {
+  if (T < 0 || K <= 0 || E_global <= 0) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int j = 0; j < K; ++j) {
+      const int g = topk_ids[(size_t)t * K + j];
+      int loc = -1;
+      if ((num_local_tokens < 0 || t < num_local_tokens) && g >= 0 && g < E_global) loc = expert_map ? expert_map[g] : g;
+      local_ids[(size_t)t * K + j] = loc;
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Token -> expert sort                                                       */
 /* ------------------------------------------------------------------------- */

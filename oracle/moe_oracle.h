@@ -48,6 +48,8 @@ int orc_route_topk(const float* logits, int T, int E, int topk, int score, int r
 int orc_route_grouped_topk(const float* logits, const float* bias, int T, int E, int topk, int n_group,
                            int topk_group, int score, int renormalize, float scaling, int n_shared,
                            float shared_weight, int32_t* topk_ids, float* topk_weights);
+int orc_map_experts(const int32_t* topk_ids, const int32_t* expert_map, int num_local_tokens, int T, int K,
+                    int E_global, int32_t* local_ids);
 
 /* ---- token -> expert sort, padded per expert to block_m rows ---- */
 int64_t orc_sort_capacity(int T, int K, int E_total, int block_m);

@@ -27,6 +27,9 @@ Which test pins which oracle function (tests/test_oracle_*.py, all CPU):
       numpy sort/lexsort on random inputs with exact ties; slots from at most
       topk_group groups; weights are the unbiased scores and sum to the scaling
       factor; a uniform bias shift keeps the ids.
+  orc_map_experts
+      numpy fancy indexing of the map; the expert-parallel shares of a layer (each
+      device's local weights, local ids) add up to the whole layer's output.
   orc_align_sort
       numpy.argsort(kind="stable") of the flattened ids; offsets multiples of
       block_m; every slot exactly once.
@@ -108,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.orc_mx_shared_exp.argtypes = [ctypes.c_float]
         L.orc_route_topk.restype = I
         L.orc_route_topk.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, P, P]
+        L.orc_map_experts.restype = I
+        L.orc_map_experts.argtypes = [P, P, I, I, I, I, P]
         L.orc_route_grouped_topk.restype = I
         L.orc_route_grouped_topk.argtypes = [P, P, I, I, I, I, I, I, I, ctypes.c_float, I, ctypes.c_float, P, P]
         L.orc_sort_capacity.restype = ctypes.c_int64
@@ -208,6 +213,20 @@ def route_grouped_topk(logits: np.ndarray, topk: int, n_group: int, topk_group: 
     if rc:
         raise ValueError("orc_route_grouped_topk: bad arguments")
     return ids, w
+
+
+def map_experts(topk_ids: np.ndarray, expert_map: np.ndarray | None, E_global: int,
+                num_local_tokens: int | None = None) -> np.ndarray:
+    """Local ids of an expert-parallel share (see orc_map_experts)."""
+    topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    T, K = topk_ids.shape
+    m = None if expert_map is None else np.ascontiguousarray(expert_map, dtype=np.int32)
+    out = np.empty((T, K), np.int32)
+    rc = lib().orc_map_experts(_ptr(topk_ids), _ptr(m), -1 if num_local_tokens is None else num_local_tokens, T, K,
+                               E_global, _ptr(out))
+    if rc:
+        raise ValueError("orc_map_experts: bad arguments")
+    return out
 
 
 def sort_capacity(T: int, K: int, E_total: int, block_m: int) -> int:
