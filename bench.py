@@ -116,15 +116,20 @@ def traffic_from_profiles(workload_name: str):
     return float(vals["TRAFFIC_BYTES_PER_LAUNCH"])
 
 
-def cpu_baseline(w, data, seconds: float, act_host: dict | None = None):
+def cpu_baseline(w, data, seconds: float, act_host: dict | None = None, emap=None):
     """The oracle, as it stands, on a bounded sample of the same workload (rank 0, N=1).
-    act_host: SwiGLU-OAI settings and host bias arrays when the layer uses them."""
+    act_host: SwiGLU-OAI settings and host bias arrays when the layer uses them; emap: the
+    expert map of an expert-parallel share (data then holds the local experts only)."""
     import numpy as np
 
     from oracle import oracle as orc
 
     ids, wts = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
-    L = orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
+    E_loc = w.E_total
+    if emap is not None:
+        ids = orc.map_experts(ids, emap, w.E_total)
+        E_loc = int(emap.max()) + 1
+    L = orc.Layer(w.H, w.I, E_loc, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
                   data["w2_scale"], **(act_host or {}))
     per_call = max(1, min(w.T, 64))
     done, t0, start = 0, time.perf_counter(), 0
@@ -159,6 +164,9 @@ def main() -> int:
     ap.add_argument("--act", choices=["silu", "swiglu-oai"], default="silu",
                     help="swiglu-oai: SwiGLU-OAI (alpha 1.702, beta 1, limit 7) with interleaved gate/up rows and "
                          "seeded bf16 biases on both projections (the gpt-oss layer form)")
+    ap.add_argument("--ep-share", type=int, default=1,
+                    help="G > 1: time device 0's share of an expert-parallel layer over G devices (experts "
+                         "[0, E/G) plus the replicated shared experts; all T tokens routed globally)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=10,
@@ -211,13 +219,26 @@ def main() -> int:
                    w1_bias=bf(synth.interleave_rows(b1, w.I)), w2_bias=bf(b2))
         act_host = dict(act=1, alpha=1.702, beta=1.0, limit=7.0, gate_up_interleaved=True,
                         w1_bias=synth.interleave_rows(b1, w.I), w2_bias=b2)
+    emap = None
+    if args.ep_share > 1:
+        G = args.ep_share
+        if w.E % G:
+            print(f"bench.py: --ep-share {G} needs the expert count to split into {G} shares", file=sys.stderr)
+            return 2
+        mine = np.concatenate([np.arange(w.E // G), w.E + np.arange(w.n_shared)])
+        m = np.full(w.E_total, -1, np.int32)
+        m[mine] = np.arange(len(mine), dtype=np.int32)
+        emap = torch.from_numpy(m).to(dev)
+        data = dict(data, **{k: np.ascontiguousarray(data[k][mine]) for k in ("w1", "w1_scale", "w2", "w2_scale")})
+        wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale"))
+        copies = args.weight_copies or (1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1))
     layers = []
     for _ in range(copies):
         layers.append(B.MoELayer(t(data["w1"]), t(data["w1_scale"]), t(data["w2"]), t(data["w2_scale"]), H=w.H,
                                  I=w.I, E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
                                  score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                                  n_shared=w.n_shared, shared_weight=w.shared_weight, block_m=args.block_m,
-                                 tiled=args.layout == "tiled", grouped=grouped, act=act))
+                                 tiled=args.layout == "tiled", grouped=grouped, act=act, expert_map=emap))
     x = torch.from_numpy(data["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     logits = t(data["logits"])
     hip = _hip()
@@ -294,7 +315,9 @@ def main() -> int:
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
                    "weight_layout": args.layout,
                    "router_kind": "grouped (8 groups, 4 kept, bias, scaling 2.5)" if grouped else "plain top-k",
-                   "activation": "swiglu-oai, interleaved w13, biases" if act else "silu-and-mul"},
+                   "activation": "swiglu-oai, interleaved w13, biases" if act else "silu-and-mul",
+                   "ep_share": (f"device 0 of EP{args.ep_share}: {w.E // args.ep_share} routed + {w.n_shared} "
+                                f"shared experts; value = T / this device's step time") if emap is not None else None},
         "roofline": roof,
         "step_breakdown_us": {"gpu_step": round(gpu_ms * 1e3 / args.steps, 2),
                               "stage1_gemm": round(g1_ms * 1e3, 2), "a2_quant+stage2_gemm": round(float(np.mean(g2)) * 1e3, 2),
@@ -311,7 +334,8 @@ def main() -> int:
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds, act_host)
+        result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds, act_host,
+                                              None if emap is None else emap.cpu().numpy())
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

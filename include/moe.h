@@ -143,6 +143,28 @@ moe_status moe_route_grouped_topk(const float* router_logits, const float* corre
                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_map_experts -- this device's share of an expert-parallel layer.
+ *
+ * The pages hand an expert map to the fused kernel as its expert mask, with the count of
+ * valid token rows ([rocm_aiter_moe] AiterExperts.apply: expert_mask=expert_map,
+ * num_local_tokens = expert_tokens_meta.expert_num_tokens).  For every slot (t, j):
+ *   local_ids[t, j] = expert_map[topk_ids[t, j]]  if topk_ids[t, j] is in [0, E_global)
+ *                                                 and t < *num_local_tokens,
+ *                   = -1                          otherwise.
+ * expert_map [E_global] int32 holds each global expert's local id on this device (its
+ * row in this device's w1/w2) or -1; NULL means the identity.  num_local_tokens is a
+ * device int32 scalar or NULL (every row valid).  Feed local_ids to moe_align_sort and
+ * moe_experts_forward with E_total = the local expert count: slots with -1 are skipped
+ * and the layer's output is this device's partial sum (rows with no local slot are 0).
+ *   topk_ids [T, K] int32 (global ids);  local_ids [T, K] int32 (written)
+ * Limits: T >= 0, 1 <= K <= 64, 1 <= E_global <= 2^20, T*K < 2^31; map entries must be
+ * -1 or valid local ids.  Errors: MOE_EINVAL for arguments outside these limits, NULL or
+ * misaligned pointers.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_map_experts(const int32_t* topk_ids, const int32_t* expert_map, const int32_t* num_local_tokens,
+                           int T, int K, int E_global, int32_t* local_ids, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_align_sort -- stable token->expert sort padded to the GEMM row tile.
  *
  * The flattened slots s = t*K + j (K = slots per token, routed + shared) are grouped by

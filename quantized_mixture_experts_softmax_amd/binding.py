@@ -21,7 +21,7 @@ A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
 ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
 EXPORTED = [
-    "moe_route_topk", "moe_route_grouped_topk", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
+    "moe_route_topk", "moe_route_grouped_topk", "moe_map_experts", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
     "moe_tiled_weight_bytes", "moe_tile_weights",
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int
         L.moe_route_topk.restype = S
         L.moe_route_topk.argtypes = [P, I, I, I, I, I, I, ctypes.c_float, P, P, P]
+        L.moe_map_experts.restype = S
+        L.moe_map_experts.argtypes = [P, P, P, I, I, I, P, P]
         L.moe_route_grouped_topk.restype = S
         L.moe_route_grouped_topk.argtypes = [P, P, I, I, I, I, I, I, I, ctypes.c_float, I, ctypes.c_float, P, P, P]
         L.moe_sort_capacity.restype = ctypes.c_size_t
@@ -204,6 +206,23 @@ def moe_route_grouped_topk(router_logits: torch.Tensor, topk: int, num_expert_gr
                                         topk_group, SCORE[score], int(renormalize), routed_scaling_factor, n_shared,
                                         shared_weight, _ptr(topk_ids), _ptr(topk_weights), _stream(stream, dev)))
     return topk_ids, topk_weights
+
+
+def moe_map_experts(topk_ids: torch.Tensor, expert_map: torch.Tensor | None, E_global: int,
+                    num_local_tokens: torch.Tensor | None = None, out=None, stream=None) -> torch.Tensor:
+    """Local ids of this device's expert-parallel share (-1: not here)."""
+    dev = _dev(topk_ids)
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2
+    for t in (expert_map, num_local_tokens):
+        if t is not None:
+            assert t.dtype == torch.int32
+            _dev(t)
+    T, K = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _check(lib().moe_map_experts(_ptr(topk_ids), _ptr(expert_map), _ptr(num_local_tokens), T, K, E_global,
+                                 _ptr(out), _stream(stream, dev)))
+    return out
 
 
 def moe_align_sort(topk_ids: torch.Tensor, E_total: int, block_m: int, out: dict | None = None, stream=None) -> dict:
@@ -350,11 +369,16 @@ class MoELayer:
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
-                 tiled: bool = False, grouped: dict | None = None, act: dict | None = None):
+                 tiled: bool = False, grouped: dict | None = None, act: dict | None = None,
+                 expert_map: torch.Tensor | None = None):
         """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights).
         grouped = dict(num_expert_group, topk_group, correction_bias (tensor or None),
         routed_scaling_factor) routes with moe_route_grouped_topk (then moe_align_sort).
-        act: activation, row order and biases, as for forward_args (None: SiLU-and-mul)."""
+        act: activation, row order and biases, as for forward_args (None: SiLU-and-mul).
+        expert_map (int32 [E + n_shared] global -> local id or -1): this device's share of an
+        expert-parallel layer; the weights hold the local experts only, the router runs over
+        the global experts and moe_map_experts turns its ids into local ones."""
+        self.E_local = w1.shape[0]
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
             w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
@@ -370,20 +394,24 @@ class MoELayer:
         self.block_m = block_m
         self.grouped = grouped
         self.act = act
+        self.expert_map = expert_map
+        if expert_map is None:
+            assert self.E_local == self.E_total, "weights hold E + n_shared experts (or pass expert_map)"
         self._bufs: dict = {}
 
     def _buffers(self, T: int, dev):
         key = (T, str(dev))
         if key not in self._bufs:
             bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total)
-            cap = moe_sort_capacity(T, self.K, self.E_total, bm)
+            cap = moe_sort_capacity(T, self.K, self.E_local, bm)
             b = dict(
                 bm=bm,
                 ids=torch.empty((T, self.K), dtype=torch.int32, device=dev),
+                ids_global=torch.empty((T, self.K), dtype=torch.int32, device=dev),
                 w=torch.empty((T, self.K), dtype=torch.float32, device=dev),
                 sort=dict(
-                    expert_counts=torch.empty(self.E_total, dtype=torch.int32, device=dev),
-                    expert_offsets=torch.empty(self.E_total + 1, dtype=torch.int32, device=dev),
+                    expert_counts=torch.empty(self.E_local, dtype=torch.int32, device=dev),
+                    expert_offsets=torch.empty(self.E_local + 1, dtype=torch.int32, device=dev),
                     sorted_slots=torch.empty(cap, dtype=torch.int32, device=dev),
                     block_expert=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
                     num_padded=torch.empty(1, dtype=torch.int32, device=dev)),
@@ -399,7 +427,12 @@ class MoELayer:
     def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
         T = x.shape[0]
         b = self._buffers(T, x.device)
-        if self.grouped is None:
+        if self.expert_map is not None:
+            moe_route_topk(router_logits, self.topk, self.score, True, self.n_shared, self.shared_weight,
+                           b["ids_global"], b["w"], stream)
+            moe_map_experts(b["ids_global"], self.expert_map, self.E_total, None, b["ids"], stream)
+            moe_align_sort(b["ids"], self.E_local, b["bm"], b["sort"], stream)
+        elif self.grouped is None:
             moe_route_align(router_logits, self.topk, b["bm"], self.score, True, self.n_shared, self.shared_weight,
                             b["ids"], b["w"], b["sort"], stream)
         else:
@@ -413,5 +446,5 @@ class MoELayer:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
         out, b["workspace"] = moe_experts_forward(
             x, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"], self.wfmt, self.afmt,
-            b["bm"], self.E_total, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
+            b["bm"], self.E_local, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
         return out

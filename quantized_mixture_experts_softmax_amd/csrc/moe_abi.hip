@@ -181,6 +181,20 @@ moe_status moe_route_grouped_topk(const float* router_logits, const float* corre
                     "moe_route_grouped_topk launch");
 }
 
+moe_status moe_map_experts(const int32_t* topk_ids, const int32_t* expert_map, const int32_t* num_local_tokens,
+                           int T, int K, int E_global, int32_t* local_ids, hipStream_t stream) {
+  const char* fn = "moe_map_experts";
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (K < 1 || K > 64) return fail(MOE_EINVAL, "%s: K must be in [1, 64] (got %d)", fn, K);
+  if (E_global < 1 || E_global > (1 << 20)) return fail(MOE_EINVAL, "%s: E_global must be in [1, 2^20] (got %d)", fn, E_global);
+  if (T > 0 && (!topk_ids || !local_ids)) return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if ((long long)T * K > 0x7FFFFFFFLL) return fail(MOE_EINVAL, "%s: T*K too large", fn);
+  if (!aligned(topk_ids, 4) || !aligned(expert_map, 4) || !aligned(num_local_tokens, 4) || !aligned(local_ids, 4))
+    return fail(MOE_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+  return hip_status(moe::launch_map_experts(topk_ids, expert_map, num_local_tokens, T, K, E_global, local_ids, stream),
+                    "moe_map_experts launch");
+}
+
 size_t moe_sort_capacity(int T, int K, int E_total, int block_m) {
   if (T < 0 || K < 0 || E_total < 0 || block_m < 1) return 0;
   return (size_t)T * K + (size_t)E_total * (block_m - 1);

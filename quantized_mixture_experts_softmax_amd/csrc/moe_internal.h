@@ -66,6 +66,8 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int sc
 hipError_t launch_route_grouped_topk(const float* logits, const float* bias, int T, int E, int topk, int n_group,
                                      int topk_group, int score, int renorm, float scaling, int n_shared,
                                      float shared_w, int32_t* ids, float* weights, hipStream_t stream);
+hipError_t launch_map_experts(const int32_t* ids, const int32_t* emap, const int32_t* n_valid, int T, int K,
+                              int E_global, int32_t* out, hipStream_t stream);
 hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, int32_t* counts, int32_t* offsets,
                              int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 // Router + align-sort in a single one-workgroup launch; only when route_sort_fusable(T, E, K)
