@@ -576,9 +576,9 @@ int orc_num_threads(void) {
  * rg = 2n, ru = 2n + 1 (the INTERLEAVE gate mode [rocm_aiter_moe]
  * mxfp4_w4a16_extra_kwargs selects for MXFP4 w4a16).  Biases are bf16 [E, 2I] in the
  * same row order ([mxfp4.py] Mxfp4MoEMethod.create_weights: w13_bias). */
-int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
+int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                const int32_t* tokens, int n_tok, uint16_t* h) {
-  if (!layer_ok(L) || n_tok < 0) return -1;
+  if (!layer_ok(L) || n_tok < 0 || (L->weight_on_input && !topk_weights)) return -1;
   const int H = L->H, I = L->I, K = L->K;
   int err = 0;
 #pragma omp parallel
@@ -605,13 +605,17 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
           for (int n = 0; n < I; ++n) hrow[n] = 0;
           continue;
         }
+        /* router weight on the input: FC1 is linear, so scaling its input by the weight
+         * scales both projections ([rocm_aiter_moe] AiterFp8TensorExperts.apply: tkw1
+         * applies topk_weights to FC1's output instead of FC2's; top-1 only) */
+        const double fc1w = L->weight_on_input ? (double)topk_weights[(size_t)t * K + j] : 1.0;
         for (int n = 0; n < I; ++n) {
           const int rg = L->gate_up_interleaved ? 2 * n : n;
           const int ru = L->gate_up_interleaved ? 2 * n + 1 : I + n;
           weight_row(L->wfmt, L->w1, L->w1_scale, e, rg, 2 * I, H, wr);
-          const double g = dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + rg);
+          const double g = fc1w * dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + rg);
           weight_row(L->wfmt, L->w1, L->w1_scale, e, ru, 2 * I, H, wr);
-          const double u = dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + ru);
+          const double u = fc1w * dot(a, wr, H) + bias_at(L->w1_bias, (size_t)e * 2 * I + ru);
           hrow[n] = orc_f64_to_bf16(glu(L, g, u));
         }
       }
@@ -655,7 +659,7 @@ int orc_stage2(const orc_layer* L, const uint16_t* h, const int32_t* topk_ids, c
           err = 1;
           continue;
         }
-        const double wj = (double)topk_weights[(size_t)t * K + j];
+        const double wj = L->weight_on_input ? 1.0 : (double)topk_weights[(size_t)t * K + j];
         for (int m = 0; m < H; ++m) {
           weight_row(L->wfmt, L->w2, L->w2_scale, e, m, H, I, wr);
           orow[m] += wj * (dot(a, wr, I) + bias_at(L->w2_bias, (size_t)e * H + m));
@@ -673,7 +677,7 @@ int orc_forward(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, 
   if (!layer_ok(L) || n_tok < 0) return -1;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n_tok * L->K * L->I + 1);
   if (!h) return -1;
-  int rc = orc_stage1(L, x, topk_ids, tokens, n_tok, h);
+  int rc = orc_stage1(L, x, topk_ids, topk_weights, tokens, n_tok, h);
   if (rc == 0) rc = orc_stage2(L, h, topk_ids, topk_weights, tokens, n_tok, out);
   free(h);
   return rc;

@@ -74,14 +74,17 @@ typedef struct {
   int gate_up_interleaved;    /* 0: w13 rows [gate_0..gate_{I-1}, up_0..up_{I-1}]; 1: gate_n, up_n alternate */
   const uint16_t* w1_bias;    /* bf16 [E_total][2I] in w13 row order, or NULL */
   const uint16_t* w2_bias;    /* bf16 [E_total][H], or NULL */
+  int weight_on_input;        /* 1: the top-k weight scales the gate/up projections (stage 1)
+                                 and the sum over slots is unweighted (top-1 routing) */
 } orc_layer;
 
 /* Stage 1 for the tokens listed in `tokens` (n_tok of them):
  *   h[(i*K + j)*I + n] = bf16( act(g, u) ) for slot j of token tokens[i], g and u the
- *   gate and up rows' dot products plus their biases.
+ *   gate and up rows' dot products (times the slot's top-k weight when weight_on_input;
+ *   topk_weights is read only then) plus their biases.
  * Activations are x (bf16) or, for quantised formats, x quantised and dequantised
  * per row with the layer's activation format. */
-int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids,
+int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                const int32_t* tokens, int n_tok, uint16_t* h);
 
 /* Stage 2: takes the per-slot intermediate h (bf16, layout as orc_stage1 writes

@@ -27,6 +27,9 @@ Which test pins which oracle function (tests/test_oracle_*.py, all CPU):
       numpy sort/lexsort on random inputs with exact ties; slots from at most
       topk_group groups; weights are the unbiased scores and sum to the scaling
       factor; a uniform bias shift keeps the ids.
+  router weight on the input (orc_layer.weight_on_input, top-1)
+      weight 1 equals the ordinary layer bit for bit; weight w equals W2 . act(w Wg a,
+      w Wu a) written with numpy matmul on weights decoded from the literal tables.
   orc_map_experts
       numpy fancy indexing of the map; the expert-parallel shares of a layer (each
       device's local weights, local ids) add up to the whole layer's output.
@@ -121,9 +124,8 @@ def lib() -> ctypes.CDLL:
         L.orc_align_sort.argtypes = [P, I, I, I, I, P, P, P, P, P]
         L.orc_quant_act.restype = I
         L.orc_quant_act.argtypes = [P, I, I, I, P, P]
-        for fn in ("orc_stage1",):
-            getattr(L, fn).restype = I
-            getattr(L, fn).argtypes = [P, P, P, P, I, P]
+        L.orc_stage1.restype = I
+        L.orc_stage1.argtypes = [P, P, P, P, P, I, P]
         L.orc_stage2.restype = I
         L.orc_stage2.argtypes = [P, P, P, P, P, I, P]
         L.orc_forward.restype = I
@@ -281,6 +283,7 @@ class _Layer(ctypes.Structure):
         ("act", ctypes.c_int), ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("limit", ctypes.c_double),
         ("gate_up_interleaved", ctypes.c_int),
         ("w1_bias", ctypes.c_void_p), ("w2_bias", ctypes.c_void_p),
+        ("weight_on_input", ctypes.c_int),
     ]
 
 
@@ -307,6 +310,7 @@ class Layer:
     gate_up_interleaved: bool = False
     w1_bias: np.ndarray | None = None  # bf16 bits [E_total, 2I] in w1 row order
     w2_bias: np.ndarray | None = None  # bf16 bits [E_total, H]
+    weight_on_input: bool = False      # top-k weight on FC1 (top-1 routing), unweighted sum
 
     def _c(self) -> _Layer:
         for a in (self.w1, self.w1_scale, self.w2, self.w2_scale, self.w1_bias, self.w2_bias):
@@ -316,7 +320,7 @@ class Layer:
         return _Layer(self.H, self.I, self.E_total, self.K, self.wfmt, self.afmt,
                       _ptr(self.w1), _ptr(self.w1_scale), _ptr(self.w2), _ptr(self.w2_scale),
                       self.act, self.alpha, self.beta, self.limit, int(self.gate_up_interleaved),
-                      _ptr(self.w1_bias), _ptr(self.w2_bias))
+                      _ptr(self.w1_bias), _ptr(self.w2_bias), int(self.weight_on_input))
 
 
 def _tokens(T: int, tokens) -> np.ndarray:
@@ -325,13 +329,15 @@ def _tokens(T: int, tokens) -> np.ndarray:
     return np.ascontiguousarray(tokens, dtype=np.int32)
 
 
-def stage1(L: Layer, x_bf16: np.ndarray, topk_ids: np.ndarray, tokens=None) -> np.ndarray:
+def stage1(L: Layer, x_bf16: np.ndarray, topk_ids: np.ndarray, tokens=None, topk_weights=None) -> np.ndarray:
+    """topk_weights: needed (and used) only when L.weight_on_input."""
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    tw = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
     tk = _tokens(x_bf16.shape[0], tokens)
     h = np.empty((len(tk) * L.K, L.I), np.uint16)
     c = L._c()
-    rc = lib().orc_stage1(ctypes.byref(c), _ptr(x_bf16), _ptr(topk_ids), _ptr(tk), len(tk), _ptr(h))
+    rc = lib().orc_stage1(ctypes.byref(c), _ptr(x_bf16), _ptr(topk_ids), _ptr(tw), _ptr(tk), len(tk), _ptr(h))
     if rc:
         raise ValueError("orc_stage1 failed")
     return h

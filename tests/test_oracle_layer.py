@@ -224,3 +224,34 @@ def test_shared_expert_slot(orc):
     L1 = orc.Layer(wl.H, wl.I, wl.E_total, 1, wl.wfmt, wl.afmt, data["w1"], data["w1_scale"], data["w2"], data["w2_scale"])
     shared = orc.forward(L1, data["x"], np.full((4, 1), 4, np.int32), np.ones((4, 1), np.float32))
     assert np.array_equal(out, routed + shared)
+
+
+@pytest.mark.parametrize("wfmt,afmt", [(synth.W_MXFP4, synth.A_BF16), (synth.W_FP8_CHANNEL, synth.A_FP8_TOKEN)])
+def test_router_weight_on_input(orc, wfmt, afmt):
+    """Router weight on the input (top-1): weight 1 is the ordinary layer bit for bit;
+    weight w is W2 . act(w Wg a, w Wu a), unweighted -- written with numpy matmul on
+    weights decoded from the literal tables -- and differs from w times the ordinary
+    layer (the activation is not linear)."""
+    wl = tiny(wfmt, afmt, T=6, H=256, I=128, E=3, k=1)
+    data = synth.make_all(wl)
+    ids = np.array([[2], [0], [1], [2], [2], [0]], np.int32)
+    ones = np.ones((6, 1), np.float32)
+    plain = layer_of(orc, wl, data)
+    tk = orc.Layer(wl.H, wl.I, wl.E_total, 1, wfmt, afmt, data["w1"], data["w1_scale"], data["w2"], data["w2_scale"],
+                   weight_on_input=True)
+    assert np.array_equal(orc.forward(tk, data["x"], ids, ones), orc.forward(plain, data["x"], ids, ones))
+    wt = np.array([[0.25], [0.8], [1.5], [0.5], [0.125], [1.0]], np.float32)
+    got = orc.forward(tk, data["x"], ids, wt)
+    W1 = decode_weights(wfmt, data["w1"], data["w1_scale"], 2 * wl.I, wl.H)
+    W2 = decode_weights(wfmt, data["w2"], data["w2_scale"], wl.H, wl.I)
+    X = synth.bf16_bits_to_f32(data["x"]).astype(np.float64)
+    for t in range(6):
+        e, w = ids[t, 0], float(wt[t, 0])
+        a = quant_dequant(X[t], afmt)
+        gate = w * np.matmul(W1[e, :wl.I], a)
+        up = w * np.matmul(W1[e, wl.I:], a)
+        h = quant_dequant(bf16_round(gate / (1.0 + np.exp(-gate)) * up), afmt)
+        ref = np.matmul(W2[e], h)
+        assert np.max(np.abs(got[t] - ref)) <= 1e-3 * np.sqrt(np.mean(ref ** 2))
+    weighted_out = orc.forward(plain, data["x"], ids, wt)
+    assert not np.allclose(got, weighted_out, rtol=1e-3)
