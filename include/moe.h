@@ -272,6 +272,10 @@ typedef struct moe_forward_args {
   const uint16_t* w1_bias;                       /* bf16 [E_total, 2I] in w1 row order, or NULL */
   const uint16_t* w2_bias;                       /* bf16 [E_total, H], or NULL ([mxfp4.py]
                                                     create_weights: w13_bias, w2_bias) */
+  int apply_router_weight_on_input;              /* 1: topk_weights scale both stage-1
+                                                    projections and the sum over slots is
+                                                    unweighted; needs K == 1 ([rocm_aiter_moe]
+                                                    AiterFp8TensorExperts.apply: tkw1) */
 } moe_forward_args;
 
 /* Byte offsets into the workspace (each 256-byte aligned); 0 size = not used. */

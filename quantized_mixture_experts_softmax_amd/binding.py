@@ -52,6 +52,7 @@ class ForwardArgs(ctypes.Structure):
         ("act_alpha", ctypes.c_float), ("act_beta", ctypes.c_float), ("act_limit", ctypes.c_float),
         ("gate_up_interleaved", ctypes.c_int),
         ("w1_bias", ctypes.c_void_p), ("w2_bias", ctypes.c_void_p),
+        ("apply_router_weight_on_input", ctypes.c_int),
     ]
 
 
@@ -300,7 +301,8 @@ def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weigh
                  afmt: int, block_m: int, E_total: int, I: int, out=None, workspace=None, a1_codes=None,
                  a1_scales=None, weight_layout: int = LAYOUT_CANONICAL, act: dict | None = None) -> ForwardArgs:
     """act: None (SiLU-and-mul) or dict(kind=ACT_SILU | ACT_SWIGLU_OAI, alpha, beta, limit,
-    interleaved, w1_bias, w2_bias) -- biases are bf16 tensors [E, 2I] / [E, H] or None."""
+    interleaved, w1_bias, w2_bias, weight_on_input) -- biases are bf16 tensors [E, 2I] /
+    [E, H] or None; weight_on_input puts the top-1 weight on the stage-1 projections."""
     T, H = hidden_states.shape
     K = topk_ids.shape[1]
     a = ForwardArgs()
@@ -309,6 +311,7 @@ def forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weigh
     a.wfmt, a.afmt, a.act = wfmt, afmt, act.get("kind", ACT_SILU)
     a.act_alpha, a.act_beta, a.act_limit = act.get("alpha", 1.702), act.get("beta", 1.0), act.get("limit", 7.0)
     a.gate_up_interleaved = int(bool(act.get("interleaved", False)))
+    a.apply_router_weight_on_input = int(bool(act.get("weight_on_input", False)))
     for name, n in (("w1_bias", 2 * I), ("w2_bias", H)):
         b = act.get(name)
         if b is not None:

@@ -454,6 +454,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
             const int row = m * 16 + 4 * g + rr;
             float v = acc[m][t][rr];
             if (WF == kWFp8Channel) v = v * lds_as[0][row] * wsc[t];
+            if (EPI && p.weight_on_input) v *= fc1_weight(p, p.sorted_slots[b * BM + row]);
             v += bsv[t];
             const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
             if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
@@ -474,6 +475,11 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
               const float as = lds_as[0][row];
               gv = gv * as * wsc[t];
               uv = uv * as * wsc[tu];
+            }
+            if (EPI && p.weight_on_input) {
+              const float fw = fc1_weight(p, p.sorted_slots[b * BM + row]);
+              gv *= fw;
+              uv *= fw;
             }
             gv += bsv[t];
             uv += bsv[tu];
@@ -744,6 +750,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                 float v = acc[m][t][rr];
                 if constexpr (WF == kWFp8Channel)
                   v = v * (o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f) * ws;
+                if (EPI && p.weight_on_input) v *= fc1_weight(p, p.sorted_slots[b * BM + row]);
                 v += bs;
                 const float up = __shfl_xor(v, 1, kWave);
                 if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
@@ -768,6 +775,11 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                   const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f;
                   gv = gv * as * wg;
                   uv = uv * as * wu;
+                }
+                if (EPI && p.weight_on_input) {
+                  const float fw = fc1_weight(p, p.sorted_slots[b * BM + row]);
+                  gv *= fw;
+                  uv *= fw;
                 }
                 gv += bg;
                 uv += bu;
@@ -1120,6 +1132,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               const int row = 4 * g + rr;
               float v = acc[t][rr];
               if constexpr (WF == kWFp8Channel) v = v * ((const float*)lds_sc)[row] * csc[t];
+              if (EPI && p.weight_on_input) v *= fc1_weight(p, lds_slot[row]);
               if (EPI && p.bias) v += bias_of(p, e, trow_of(u, t) + li);
               const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
               if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
@@ -1135,6 +1148,11 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               const float as = ((const float*)lds_sc)[row];
               gv = gv * as * csc[0];
               uv = uv * as * csc[1];
+            }
+            if (EPI && p.weight_on_input) {
+              const float fw = fc1_weight(p, lds_slot[row]);
+              gv *= fw;
+              uv *= fw;
             }
             if (EPI && p.bias) {
               gv += bias_of(p, e, trow_of(u, 0) + li);
@@ -1227,7 +1245,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
 }
 
 // out[t, :] = bf16( sum_{j ascending} w[t, j] * ybuf[t*K + j, :] ), slots with invalid
-// ids skipped.  Each product is rounded to fp32 before it is added (no fused
+// ids skipped; w = 1 when wts is NULL (router weight applied on the input).  Each product is rounded to fp32 before it is added (no fused
 // multiply-add), the same arithmetic as weighting each row first and summing after.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf, const int32_t* __restrict__ ids,
                                                       const float* __restrict__ wts, int T, int K, int H, int E,
@@ -1241,7 +1259,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < K; ++j) {
     const int e = ids[(size_t)t * K + j];
     if (e < 0 || e >= E) continue;
-    const float w = wts[(size_t)t * K + j];
+    const float w = wts ? wts[(size_t)t * K + j] : 1.0f;
     const f32x4 y = *(const f32x4*)(ybuf + ((size_t)t * K + j) * H + c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1351,7 +1369,7 @@ static hipError_t launch_bm_wl(int bm, const GemmParams& p, hipStream_t stream) 
 
 template <int STAGE, int WF, int AF>
 static hipError_t launch_bm(int bm, const GemmParams& p, hipStream_t stream) {
-  const bool general = p.bias || (STAGE == 1 && (p.act != kActSilu || p.interleaved));
+  const bool general = p.bias || (STAGE == 1 && (p.act != kActSilu || p.interleaved || p.weight_on_input));
   if (general)
     return p.weight_layout ? launch_bm_wl<STAGE, WF, AF, 1, 1>(bm, p, stream)
                            : launch_bm_wl<STAGE, WF, AF, 0, 1>(bm, p, stream);

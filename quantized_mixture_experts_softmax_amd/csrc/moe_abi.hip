@@ -73,6 +73,10 @@ moe_status check_shapes(const moe_forward_args* a) {
     return fail(MOE_EUNSUPPORTED, "activation %d is not implemented (SiLU-and-mul, SwiGLU-OAI)", (int)a->act);
   if (a->gate_up_interleaved != 0 && a->gate_up_interleaved != 1)
     return fail(MOE_EINVAL, "gate_up_interleaved must be 0 or 1 (got %d)", a->gate_up_interleaved);
+  if (a->apply_router_weight_on_input != 0 && a->apply_router_weight_on_input != 1)
+    return fail(MOE_EINVAL, "apply_router_weight_on_input must be 0 or 1 (got %d)", a->apply_router_weight_on_input);
+  if (a->apply_router_weight_on_input && a->K != 1)
+    return fail(MOE_EINVAL, "the router weight goes on the input only with one slot per token (K = %d)", a->K);
   if (a->gate_up_interleaved && a->wfmt == MOE_W_FP8_BLOCK128)
     return fail(MOE_EUNSUPPORTED, "interleaved gate/up rows would split FP8 128x128 scale blocks");
   if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
@@ -358,6 +362,7 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.h = h;
   p.interleaved = a->gate_up_interleaved;
   p.bias = a->w1_bias;
+  p.weight_on_input = a->apply_router_weight_on_input;
   if ((e = prof_mark(0, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
   e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
@@ -388,12 +393,14 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.ybuf = ybuf;
   p.interleaved = 0;
   p.bias = a->w2_bias;
+  p.weight_on_input = 0;
   e = moe::launch_gemm(2, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 2");
   if ((e = prof_mark(2, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
 
   // ordered top-k combine
-  e = moe::launch_combine(ybuf, a->topk_ids, a->topk_weights, a->T, a->K, a->H, a->E_total, a->out, stream);
+  e = moe::launch_combine(ybuf, a->topk_ids, a->apply_router_weight_on_input ? nullptr : a->topk_weights, a->T, a->K,
+                          a->H, a->E_total, a->out, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: combine");
   return hip_status(prof_mark(3, stream), "moe_experts_forward: profiling event");
 }

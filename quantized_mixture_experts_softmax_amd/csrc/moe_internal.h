@@ -40,6 +40,7 @@ struct GemmParams {
   float act_alpha, act_beta, act_limit;
   int interleaved;     // stage 1: w13 rows alternate gate_n, up_n (else gate rows, then up rows)
   const uint16_t* bias;
+  int weight_on_input;  // stage 1: the slot's top-k weight scales both projections (top-1)
 };
 
 constexpr int kActSilu = 0, kActSwigluOai = 1;
@@ -54,6 +55,13 @@ __device__ __forceinline__ float glu_act(const GemmParams& p, float g, float u) 
     u = fminf(fmaxf(u, -p.act_limit), p.act_limit);
   }
   return g / (1.0f + __expf(-p.act_alpha * g)) * (u + p.act_beta);
+}
+
+// Stage-1 factor of a sorted row's projections: its slot's top-k weight when the router
+// weight goes on the input, else 1 (pad rows: 0, their activations are zero anyway).
+__device__ __forceinline__ float fc1_weight(const GemmParams& p, int slot) {
+  if (!p.weight_on_input) return 1.0f;
+  return slot < p.T * p.slots_per_token ? p.topk_weights[slot] : 0.0f;
 }
 
 // bf16 bias of weight row `row` of expert e (0 without a bias tensor).

@@ -46,7 +46,8 @@ def layer_for(w: synth.Workload, data: dict, act: dict | None = None) -> orc.Lay
     return orc.Layer(w.H, w.I, w.E_total, w.K, w.wfmt, w.afmt, data["w1"], data["w1_scale"], data["w2"],
                      data["w2_scale"], act=a.get("kind", 0), alpha=a.get("alpha", 1.702), beta=a.get("beta", 1.0),
                      limit=a.get("limit", 7.0), gate_up_interleaved=bool(a.get("interleaved", False)),
-                     w1_bias=a.get("w1_bias"), w2_bias=a.get("w2_bias"))
+                     w1_bias=a.get("w1_bias"), w2_bias=a.get("w2_bias"),
+                     weight_on_input=bool(a.get("weight_on_input", False)))
 
 
 def act_dev(act: dict | None) -> dict | None:

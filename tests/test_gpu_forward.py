@@ -76,11 +76,12 @@ def full_check(w, data, res, tokens=None, what="", act=None):
     assert np.array_equal(ids, ref_ids), f"{what}: topk_ids"
     np.testing.assert_allclose(wts, ref_w, rtol=2e-6)
     tk = np.arange(w.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
-    ref_h = orc.stage1(L, data["x"], ids, tk)
+    ref_h = orc.stage1(L, data["x"], ids, tk, topk_weights=wts)
     h_gpu = np.ascontiguousarray(h_by_slot(res, w.T, w.K, w.I).reshape(w.T, w.K, w.I)[tk].reshape(-1, w.I))
     check_h_rows(h_gpu, ref_h, what)
     ref = orc.stage2(L, ref_h, ids, wts, tk, T=w.T)  # == orc.forward on these tokens
-    acc = combine_f32(res, tk, w.K, w.H, w.E_total)
+    on_input = bool((act or {}).get("weight_on_input"))
+    acc = combine_f32(dict(res, weights=np.ones_like(wts)) if on_input else res, tk, w.K, w.H, w.E_total)
     check_rounding(res["out"][tk], acc, what)
     if w.afmt == synth.A_BF16:
         return check_output(acc, ref, f"{what} end-to-end")
@@ -181,6 +182,55 @@ def test_swiglu_oai_bias_interleave(fmt, bm, itl, bias, kind):
     say(f"act forward {what}")
     res = run_layer(w, data, block_m=bm, tiled=True, act=act)
     full_check(w, data, res, what=what, act=act)
+
+
+TKW1 = [(fmt, bm) for fmt in (W4A16, W4A4, FP8B, FP8C) for bm in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("fmt,bm", TKW1, ids=[f"w{f[0]}a{f[1]}-bm{bm}" for f, bm in TKW1])
+def test_router_weight_on_input(fmt, bm):
+    """Top-1 routing with the router weight on the input (the tkw1 form): the weight
+    scales both stage-1 projections and the combine is unweighted."""
+    if fmt == FP8B:
+        w = small(fmt, T=40, H=352, I=288, E=5, k=1, score=synth.SCORE_SIGMOID)
+    elif fmt == FP8C:
+        w = small(fmt, T=33, H=320, I=416, E=4, k=1)
+    else:
+        w = small(fmt, k=1)
+    data = synth.make_all(w)
+    act = dict(kind=0, weight_on_input=True)
+    what = f"{w.name}/bm{bm}/tkw1"
+    say(f"forward {what}")
+    res = run_layer(w, data, block_m=bm, tiled=True, act=act)
+    # with one routed slot the softmax weight is exactly 1: use sigmoid-style weights instead
+    assert res["weights"].shape[1] == 1
+    full_check(w, data, res, what=what, act=act)
+
+
+def test_router_weight_on_input_non_unit_weights():
+    """The same with weights != 1 (sigmoid scores without renormalisation)."""
+    w = synth.Workload("tk", 48, 320, 288, 6, 1, synth.W_MXFP4, synth.A_BF16, score=synth.SCORE_SIGMOID, seed=41)
+    data = synth.make_all(w)
+    wd = dev_weights(data)
+    x = bf16_dev(data["x"])
+    ids, wts = B.moe_route_topk(to_dev(data["logits"]), 1, "sigmoid", False)
+    srt = B.moe_align_sort(ids, w.E_total, 16)
+    act = dict(kind=0, weight_on_input=True)
+    out, ws = B.moe_experts_forward(x, wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], ids, wts, srt, w.wfmt,
+                                    w.afmt, 16, w.E_total, w.I, act=act)
+    torch.cuda.synchronize()
+    ids_h, wts_h = ids.cpu().numpy(), wts.cpu().numpy()
+    assert np.all(wts_h < 1.0)
+    L = layer_for(w, data, act)
+    ref = orc.forward(L, data["x"], ids_h, wts_h)
+    args = B.forward_args(x, wd["w1"], wd["w1_scale"], wd["w2"], wd["w2_scale"], ids, wts, srt, w.wfmt, w.afmt, 16,
+                          w.E_total, w.I, out, ws, act=act)
+    lay = B.moe_workspace_layout(args)
+    res = dict(ids=ids_h, weights=np.ones_like(wts_h),
+               ybuf_dev=ws[lay["ybuf_off"]:lay["ybuf_off"] + lay["ybuf_bytes"]].view(torch.float32).view(-1, w.H))
+    acc = combine_f32(res, np.arange(w.T, dtype=np.int32), 1, w.H, w.E_total)
+    check_rounding(out.view(torch.int16).cpu().numpy().view(np.uint16), acc, "tkw1 sigmoid weights")
+    check_output(acc, ref, "tkw1 sigmoid weights")
 
 
 def test_swiglu_oai_decode_full_size():
