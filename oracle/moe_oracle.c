@@ -436,6 +436,13 @@ int orc_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes
     for (int r = 0; r < rows; ++r) sc[r] = quant_group_fp8(x + (size_t)r * cols, cols, codes + (size_t)r * cols);
     return 0;
   }
+  if (fmt == ORC_A_FP8_TENSOR) {
+    /* one scale for the whole tensor: the per-group rule over all rows * cols values
+     * ([rocm_aiter_moe] QuantMethod.PER_TENSOR, AiterFp8TensorExperts) */
+    if ((long long)rows * cols > 0x7FFFFFFFLL) return -1;
+    ((float*)scales)[0] = rows ? quant_group_fp8(x, rows * cols, codes) : 1.0f;
+    return 0;
+  }
   if (fmt == ORC_A_MXFP4_G32) {
     if (cols % 32) return -1;
     uint8_t* sc = (uint8_t*)scales;
@@ -465,6 +472,7 @@ int orc_quant_act(const uint16_t* x, int rows, int cols, int fmt, uint8_t* codes
 /* Dequantised activation row (fp64) of one bf16 row of length n, through the
  * layer's activation format. */
 static int activation_row(int afmt, const uint16_t* x, int n, double* out) {
+  if (afmt == ORC_A_FP8_TENSOR) return -1; /* needs the whole tensor: tensor_rows */
   if (afmt == ORC_A_BF16) {
     for (int i = 0; i < n; ++i) out[i] = (double)orc_bf16_to_f32(x[i]);
     return 0;
@@ -488,6 +496,23 @@ static int activation_row(int afmt, const uint16_t* x, int n, double* out) {
   }
   free(codes);
   free(fsc);
+  return rc;
+}
+
+/* Per-tensor FP8 activations: the n_rows x n values given (rows[i] points at row i)
+ * quantised with one scale and dequantised into out[i * n + k]. */
+static int tensor_rows(const uint16_t* const* rows, size_t n_rows, int n, double* out) {
+  const size_t total = n_rows * (size_t)n;
+  if (total > 0x7FFFFFFFu) return -1;
+  uint16_t* buf = (uint16_t*)calloc(total + 1, sizeof(uint16_t));
+  uint8_t* codes = (uint8_t*)malloc(total + 1);
+  if (!buf || !codes) { free(buf); free(codes); return -1; }
+  for (size_t i = 0; i < n_rows; ++i) memcpy(buf + i * n, rows[i], sizeof(uint16_t) * (size_t)n);
+  float s = 1.0f;
+  int rc = orc_quant_act(buf, (int)n_rows, n, ORC_A_FP8_TENSOR, codes, &s);
+  for (size_t i = 0; rc == 0 && i < total; ++i) out[i] = orc_e4m3_value(codes[i]) * (double)s;
+  free(buf);
+  free(codes);
   return rc;
 }
 
@@ -517,8 +542,10 @@ static void weight_row(int wfmt, const uint8_t* w, const void* scale, int e, int
     const float* srow = (const float*)scale + ((size_t)e * nbn + n / 128) * (size_t)nbk;
     for (int k = 0; k < K; ++k) out[k] = orc_e4m3_value(row[k]) * (double)srow[k / 128];
   } else {
+    /* FP8 channel: scale[e][n]; FP8 tensor ([rocm_aiter_moe] AiterFp8TensorExperts,
+     * PER_TENSOR): one scale[e] per expert and projection */
     const uint8_t* row = w + ((size_t)e * N + n) * (size_t)K;
-    const double s = (double)((const float*)scale)[(size_t)e * N + n];
+    const double s = (double)((const float*)scale)[wfmt == ORC_W_FP8_TENSOR ? (size_t)e : (size_t)e * N + n];
     for (int k = 0; k < K; ++k) out[k] = orc_e4m3_value(row[k]) * s;
   }
 }
@@ -555,8 +582,8 @@ static double bias_at(const uint16_t* b, size_t i) { return b ? (double)orc_bf16
 static int layer_ok(const orc_layer* L) {
   if (!L || L->H <= 0 || L->I <= 0 || L->E_total <= 0 || L->K <= 0) return 0;
   if (L->H % 32 || L->I % 32) return 0;
-  if (L->wfmt < ORC_W_MXFP4 || L->wfmt > ORC_W_FP8_CHANNEL) return 0;
-  if (L->afmt < ORC_A_BF16 || L->afmt > ORC_A_FP8_TOKEN) return 0;
+  if (L->wfmt < ORC_W_MXFP4 || L->wfmt > ORC_W_FP8_TENSOR) return 0;
+  if (L->afmt < ORC_A_BF16 || L->afmt > ORC_A_FP8_TENSOR) return 0;
   if (L->act != ORC_ACT_SILU && L->act != ORC_ACT_SWIGLU_OAI) return 0;
   return 1;
 }
@@ -581,6 +608,17 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, c
   if (!layer_ok(L) || n_tok < 0 || (L->weight_on_input && !topk_weights)) return -1;
   const int H = L->H, I = L->I, K = L->K;
   int err = 0;
+  /* per-tensor activations: one scale over the listed tokens (the whole batch) */
+  double* a_all = NULL;
+  if (L->afmt == ORC_A_FP8_TENSOR) {
+    const uint16_t** rp = (const uint16_t**)malloc(sizeof(uint16_t*) * ((size_t)n_tok + 1));
+    a_all = (double*)malloc(sizeof(double) * ((size_t)n_tok * H + 1));
+    if (!rp || !a_all) { free(rp); free(a_all); return -1; }
+    for (int i = 0; i < n_tok; ++i) rp[i] = x + (size_t)tokens[i] * H;
+    const int rc = tensor_rows(rp, (size_t)n_tok, H, a_all);
+    free(rp);
+    if (rc) { free(a_all); return -1; }
+  }
 #pragma omp parallel
   {
     double* a = (double*)malloc(sizeof(double) * (size_t)H);
@@ -593,7 +631,9 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, c
     for (int i = 0; i < n_tok; ++i) {
       if (!a || !wr) continue;
       const int t = tokens[i];
-      if (activation_row(L->afmt, x + (size_t)t * H, H, a)) {
+      if (a_all) {
+        memcpy(a, a_all + (size_t)i * H, sizeof(double) * (size_t)H);
+      } else if (activation_row(L->afmt, x + (size_t)t * H, H, a)) {
 #pragma omp atomic write
         err = 1;
         continue;
@@ -623,6 +663,7 @@ int orc_stage1(const orc_layer* L, const uint16_t* x, const int32_t* topk_ids, c
     free(a);
     free(wr);
   }
+  free(a_all);
   return err ? -1 : 0;
 }
 
@@ -637,6 +678,19 @@ int orc_stage2(const orc_layer* L, const uint16_t* h, const int32_t* topk_ids, c
   if (!layer_ok(L) || n_tok < 0) return -1;
   const int H = L->H, I = L->I, K = L->K;
   int err = 0;
+  /* per-tensor activations: one scale over every slot row given (rows of slots that are
+   * not routed are zero and leave the amax alone) */
+  double* a_all = NULL;
+  if (L->afmt == ORC_A_FP8_TENSOR) {
+    const size_t nr = (size_t)n_tok * K;
+    const uint16_t** rp = (const uint16_t**)malloc(sizeof(uint16_t*) * (nr + 1));
+    a_all = (double*)malloc(sizeof(double) * (nr * I + 1));
+    if (!rp || !a_all) { free(rp); free(a_all); return -1; }
+    for (size_t r = 0; r < nr; ++r) rp[r] = h + r * (size_t)I;
+    const int rc = tensor_rows(rp, nr, I, a_all);
+    free(rp);
+    if (rc) { free(a_all); return -1; }
+  }
 #pragma omp parallel
   {
     double* a = (double*)malloc(sizeof(double) * (size_t)I);
@@ -654,7 +708,9 @@ int orc_stage2(const orc_layer* L, const uint16_t* h, const int32_t* topk_ids, c
       for (int j = 0; j < K; ++j) {
         const int e = topk_ids[(size_t)t * K + j];
         if (e < 0 || e >= L->E_total) continue;
-        if (activation_row(L->afmt, h + ((size_t)i * K + j) * (size_t)I, I, a)) {
+        if (a_all) {
+          memcpy(a, a_all + ((size_t)i * K + j) * (size_t)I, sizeof(double) * (size_t)I);
+        } else if (activation_row(L->afmt, h + ((size_t)i * K + j) * (size_t)I, I, a)) {
 #pragma omp atomic write
           err = 1;
           continue;
@@ -669,6 +725,7 @@ int orc_stage2(const orc_layer* L, const uint16_t* h, const int32_t* topk_ids, c
     free(a);
     free(wr);
   }
+  free(a_all);
   return err ? -1 : 0;
 }
 

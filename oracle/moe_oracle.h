@@ -25,9 +25,9 @@ extern "C" {
 #endif
 
 /* weight formats */
-enum { ORC_W_MXFP4 = 0, ORC_W_FP8_BLOCK128 = 1, ORC_W_FP8_CHANNEL = 2 };
+enum { ORC_W_MXFP4 = 0, ORC_W_FP8_BLOCK128 = 1, ORC_W_FP8_CHANNEL = 2, ORC_W_FP8_TENSOR = 3 };
 /* activation (GEMM input) formats */
-enum { ORC_A_BF16 = 0, ORC_A_MXFP4_G32 = 1, ORC_A_FP8_G128 = 2, ORC_A_FP8_TOKEN = 3 };
+enum { ORC_A_BF16 = 0, ORC_A_MXFP4_G32 = 1, ORC_A_FP8_G128 = 2, ORC_A_FP8_TOKEN = 3, ORC_A_FP8_TENSOR = 4 };
 /* router score functions */
 enum { ORC_SCORE_SOFTMAX = 0, ORC_SCORE_SIGMOID = 1 };
 

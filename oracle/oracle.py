@@ -37,7 +37,12 @@ Which test pins which oracle function (tests/test_oracle_*.py, all CPU):
       numpy.argsort(kind="stable") of the flattened ids; offsets multiples of
       block_m; every slot exactly once.
   orc_quant_act
-      brute force per element, golden worked groups, dequantised error bounds.
+      brute force per element, golden worked groups, dequantised error bounds;
+      per-tensor FP8 equals the per-row rule on the flattened tensor.
+  FP8 per-tensor weights / activations (orc_layer formats)
+      per-tensor weights equal per-channel weights with the scale broadcast over rows;
+      a one-token, one-slot batch with per-tensor activations equals per-token ones;
+      numpy brute force (torch e4m3 casts, one amax per tensor) on a whole batch.
   orc_stage1 / orc_stage2 / orc_forward
       top-1 weight-1 routing equals a dense gated MLP computed with numpy.matmul
       on weights decoded from the literal tables; closed-form all-equal example;
@@ -63,8 +68,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
-A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR = 0, 1, 2, 3
+A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 
 _lib = None
@@ -262,6 +267,9 @@ def quant_act(x_bf16: np.ndarray, fmt: int):
     elif fmt == A_FP8_TOKEN:
         codes = np.empty((rows, cols), np.uint8)
         scales = np.empty((rows,), np.float32)
+    elif fmt == A_FP8_TENSOR:
+        codes = np.empty((rows, cols), np.uint8)
+        scales = np.empty((1,), np.float32)
     elif fmt == A_MXFP4_G32:
         codes = np.empty((rows, cols // 2), np.uint8)
         scales = np.empty((rows, cols // 32), np.uint8)
@@ -329,8 +337,14 @@ def _tokens(T: int, tokens) -> np.ndarray:
     return np.ascontiguousarray(tokens, dtype=np.int32)
 
 
+def _full_batch_only(L: Layer, tokens, T: int):
+    if L.afmt == A_FP8_TENSOR and tokens is not None and not np.array_equal(np.asarray(tokens), np.arange(T)):
+        raise ValueError("per-tensor activation scales need the whole batch (tokens=None)")
+
+
 def stage1(L: Layer, x_bf16: np.ndarray, topk_ids: np.ndarray, tokens=None, topk_weights=None) -> np.ndarray:
     """topk_weights: needed (and used) only when L.weight_on_input."""
+    _full_batch_only(L, tokens, x_bf16.shape[0])
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     tw = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
@@ -346,6 +360,7 @@ def stage1(L: Layer, x_bf16: np.ndarray, topk_ids: np.ndarray, tokens=None, topk
 def stage2(L: Layer, h: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray, tokens=None,
            T: int | None = None) -> np.ndarray:
     """h: [len(tokens)*K, I] bf16 bits, slot rows in (token list, slot) order."""
+    _full_batch_only(L, tokens, topk_ids.shape[0] if T is None else T)
     h = np.ascontiguousarray(h, dtype=np.uint16)
     topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     topk_weights = np.ascontiguousarray(topk_weights, dtype=np.float32)
@@ -362,6 +377,7 @@ def stage2(L: Layer, h: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarr
 
 def forward(L: Layer, x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
             tokens=None) -> np.ndarray:
+    _full_batch_only(L, tokens, x_bf16.shape[0])
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     topk_weights = np.ascontiguousarray(topk_weights, dtype=np.float32)

@@ -32,8 +32,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
-A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR = 0, 1, 2, 3
+A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 
 
@@ -181,6 +181,8 @@ def _weight(w: Workload, N: int, K: int, seq_codes, rng_scales):
     base = 1.0 / (_FP8_RMS * math.sqrt(K))
     if w.wfmt == W_FP8_BLOCK128:
         scales = (rng_scales.uniform(0.75, 1.25, (E, (N + 127) // 128, (K + 127) // 128)) * base).astype(np.float32)
+    elif w.wfmt == W_FP8_TENSOR:
+        scales = (rng_scales.uniform(0.75, 1.25, (E,)) * base).astype(np.float32)
     else:
         scales = (rng_scales.uniform(0.75, 1.25, (E, N)) * base).astype(np.float32)
     return codes, scales
