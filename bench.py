@@ -308,8 +308,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic (seeded; random weight codes and scales, no checkpoint)",
-        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel'][w.wfmt]}-"
-                               f"{['w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token'][w.afmt]}",
+        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel', 'fp8-tensor'][w.wfmt]}-"
+                               f"{['w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token', 'a-fp8-tensor'][w.afmt]}",
                    "T": w.T, "H": w.H, "I": w.I, "experts": w.E, "shared_experts": w.n_shared, "topk": w.topk,
                    "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],

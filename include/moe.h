@@ -53,8 +53,12 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
  *                      w2 [E, H, I], w2_scale fp32 [E, ceil(H/128), ceil(I/128)]  ([rocm_aiter_moe] AiterFp8BlockExperts)
  *   MOE_W_FP8_CHANNEL  PER_TOKEN (per output channel): codes as above, w1_scale fp32 [E, 2I],
  *                      w2_scale fp32 [E, H]  ([rocm_aiter_moe] AiterFp8ChannelExperts)
+ *   MOE_W_FP8_TENSOR   PER_TENSOR: codes as above, one fp32 scale per expert and projection:
+ *                      w1_scale [E], w2_scale [E]  ([rocm_aiter_moe] AiterFp8TensorExperts)
  * In w1 rows [0, I) are the gate projection and rows [I, 2I) the up projection. */
-typedef enum moe_wfmt { MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANNEL = 2 } moe_wfmt;
+typedef enum moe_wfmt {
+  MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANNEL = 2, MOE_W_FP8_TENSOR = 3
+} moe_wfmt;
 
 /* Activation (GEMM input) formats, quantised dynamically ([rocm_aiter_moe]
  * AiterMxfp4Experts, AiterFp8BlockExperts, AiterFp8ChannelExperts):
@@ -62,8 +66,13 @@ typedef enum moe_wfmt { MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANN
  *   MOE_A_MXFP4_G32  codes uint8 [rows, cols/2] (two e2m1 per byte, low nibble = even column),
  *                    scales uint8 E8M0 [rows, cols/32]
  *   MOE_A_FP8_G128   codes e4m3fn [rows, cols], scales fp32 [rows, ceil(cols/128)]
- *   MOE_A_FP8_TOKEN  codes e4m3fn [rows, cols], scales fp32 [rows] */
-typedef enum moe_afmt { MOE_A_BF16 = 0, MOE_A_MXFP4_G32 = 1, MOE_A_FP8_G128 = 2, MOE_A_FP8_TOKEN = 3 } moe_afmt;
+ *   MOE_A_FP8_TOKEN  codes e4m3fn [rows, cols], scales fp32 [rows]
+ *   MOE_A_FP8_TENSOR codes e4m3fn [rows, cols], scales fp32 [1]: one scale for the whole
+ *                    tensor, the FP8 rule applied to all rows * cols values (the per-tensor
+ *                    activation quantisation of PER_TENSOR); used with MOE_W_FP8_TENSOR */
+typedef enum moe_afmt {
+  MOE_A_BF16 = 0, MOE_A_MXFP4_G32 = 1, MOE_A_FP8_G128 = 2, MOE_A_FP8_TOKEN = 3, MOE_A_FP8_TENSOR = 4
+} moe_afmt;
 
 /* Weight memory layout.
  *   MOE_LAYOUT_CANONICAL  the row-major tensors described under moe_wfmt.
@@ -205,8 +214,9 @@ moe_status moe_route_align(const float* router_logits, int T, int E, int topk, m
 /* ------------------------------------------------------------------------------------
  * moe_quant_act -- dynamic activation quantisation of a bf16 matrix [rows, cols].
  *
- * FP8 (e4m3fn) formats: per group (128 columns, or the whole row for MOE_A_FP8_TOKEN;
- * the last 128-group of a row may be shorter), s = amax / 448 in IEEE fp32 (s = 1 for an
+ * FP8 (e4m3fn) formats: per group (128 columns, the whole row for MOE_A_FP8_TOKEN, the
+ * whole tensor for MOE_A_FP8_TENSOR; the last 128-group of a row may be shorter),
+ * s = amax / 448 in IEEE fp32 (s = 1 for an
  * all-zero group) and code = nearest e4m3fn value of x / s (IEEE fp32 division), ties to
  * even, saturating at +-448 ([rocm_aiter_moe] AiterFp8BlockExperts: 128-grouped dynamic
  * activation scale; AiterFp8ChannelExperts: per-token dynamic scale).
@@ -216,6 +226,8 @@ moe_status moe_route_align(const float* router_logits, int T, int E, int topk, m
  * MXFP4 dynamic activations; two codes per byte as [quark_moe]
  * QuarkOCP_MX_MoEMethod.get_packed_dim).  The code's sign bit is the sign of x.
  *   x       [rows, cols] bf16;  codes / scales: layouts of moe_afmt above.
+ * MOE_A_FP8_TENSOR runs four launches (the scale slot holds the amax until the last one)
+ * and needs rows * cols < 2^31.
  * Limits: cols % 32 == 0, cols <= 65536, rows >= 0.  fmt == MOE_A_BF16 is MOE_EINVAL.
  * ---------------------------------------------------------------------------------- */
 moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
@@ -244,6 +256,7 @@ moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
  * Limits: H % 32 == 0, I % 32 == 0, H, I <= 65536, 1 <= K <= 64, E_total <= 1024,
  * block_m in {16, 32, 64, 128}; (wfmt, afmt) one of
  *   (MXFP4, BF16) (MXFP4, MXFP4_G32) (FP8_BLOCK128, FP8_G128) (FP8_CHANNEL, FP8_TOKEN)
+ *   (FP8_TENSOR, FP8_TENSOR)
  * (others: MOE_EUNSUPPORTED).  Pointers to 16-byte aligned memory.
  * ---------------------------------------------------------------------------------- */
 typedef struct moe_forward_args {

@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 SCORE = {"softmax": 0, "sigmoid": 1}
-W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL = 0, 1, 2
-A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN = 0, 1, 2, 3
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR = 0, 1, 2, 3
+A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
 EXPORTED = [
@@ -281,6 +281,8 @@ def quant_shapes(fmt: int, rows: int, cols: int):
         return (rows, cols), (rows, (cols + 127) // 128), torch.float32
     if fmt == A_FP8_TOKEN:
         return (rows, cols), (rows,), torch.float32
+    if fmt == A_FP8_TENSOR:
+        return (rows, cols), (1,), torch.float32
     raise ValueError("bf16 activations have no quantiser")
 
 

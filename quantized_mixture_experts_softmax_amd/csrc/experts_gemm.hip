@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
     ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
     wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
-    wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + trow + li] : 1.0f;
+    wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, trow + li)] : 1.0f;
   }
 
   auto load_a = [&](int c, i32x4 (&reg)[AIT]) {
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (AF == kAFp8Token) if (tid < BM) lds_as[0][tid] = s_ok ? ((const float*)p.a_scale)[s_row] : 0.0f;
+  if constexpr (AF == kAFp8Token) if (tid < BM) lds_as[0][tid] = s_ok ? ((const float*)p.a_scale)[(size_t)s_row * p.asc_rs] : 0.0f;
 
   // MFMAs of one chunk: A from LDS buffer buf, weights wr
   auto compute = [&](int buf, const WeightRegs<WF, NT>& wr) {
@@ -740,7 +740,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
           for (int t = 0; t < NT; ++t) {
             if (!tile_ok(s, t)) continue;
             const int col = tile_col(s, t), wr = tile_row(s, t) + li;
-            const float ws = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + wr] : 1.0f;
+            const float ws = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, wr)] : 1.0f;
             const float bs = (EPI && p.bias) ? bias_of(p, e, wr) : 0.0f;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                 const int row = m * 16 + 4 * g + rr;
                 float v = acc[m][t][rr];
                 if constexpr (WF == kWFp8Channel)
-                  v = v * (o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f) * ws;
+                  v = v * (o_ok[m][rr] ? ((const float*)p.a_scale)[(size_t)o_idx[m][rr] * p.asc_rs] : 0.0f) * ws;
                 if (EPI && p.weight_on_input) v *= fc1_weight(p, p.sorted_slots[b * BM + row]);
                 v += bs;
                 const float up = __shfl_xor(v, 1, kWave);
@@ -762,8 +762,8 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
             const int col = tile_col(s, t);
             if (col >= p.N) continue;
             const int tu = t + NT / 2;
-            const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + col] : 1.0f;
-            const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[(size_t)e * p.Nw + p.N + col] : 1.0f;
+            const float wg = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, col)] : 1.0f;
+            const float wu = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, p.N + col)] : 1.0f;
             const float bg = (EPI && p.bias) ? bias_of(p, e, col) : 0.0f, bu = (EPI && p.bias) ? bias_of(p, e, p.N + col) : 0.0f;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                 const int row = m * 16 + 4 * g + rr;
                 float gv = acc[m][t][rr], uv = acc[m][tu][rr];
                 if constexpr (WF == kWFp8Channel) {
-                  const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[o_idx[m][rr]] : 0.0f;
+                  const float as = o_ok[m][rr] ? ((const float*)p.a_scale)[(size_t)o_idx[m][rr] * p.asc_rs] : 0.0f;
                   gv = gv * as * wg;
                   uv = uv * as * wu;
                 }
@@ -795,13 +795,13 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
             const int row = m * 16 + 4 * g + rr;
             const int slot = p.sorted_slots[b * BM + row];
             if (slot >= TK) continue;
-            const float as = (WF == kWFp8Channel) ? ((const float*)p.a_scale)[b * BM + row] : 1.0f;
+            const float as = (WF == kWFp8Channel) ? ((const float*)p.a_scale)[(size_t)(b * BM + row) * p.asc_rs] : 1.0f;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const int col = tile_col(s, t);
               if (col >= p.N) continue;
               float v = acc[m][t][rr];
-              if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[(size_t)e * p.Nw + col];
+              if constexpr (WF == kWFp8Channel) v = v * as * ((const float*)p.w_scale)[wsc_index(p, e, col)];
               if (EPI && p.bias) v += bias_of(p, e, col);
               p.ybuf[(size_t)slot * p.N + col] = v;
             }
@@ -982,7 +982,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
           if constexpr (WF == kWFp8Block)
             r.sb[t] = ldf((const float*)p.w_scale, ((size_t)e * nbn + trow / 128) * nch + lc, tok);
           else  // channel scale of the lane's output column, carried with the step
-            r.sb[t] = ldf((const float*)p.w_scale, (size_t)e * p.Nw + trow + li, tok);
+            r.sb[t] = ldf((const float*)p.w_scale, wsc_index(p, e, trow + li), tok);
         }
       }
       if (live) {
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     } else if constexpr (AF == kAFp8Token) {
       if (tid < BM) {
         const int arow = STAGE == 1 ? lds_row[tid] : b * BM + tid;
-        sc_f = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow), arow >= 0);
+        sc_f = ldf((const float*)p.a_scale, (size_t)(arow < 0 ? 0 : arow) * p.asc_rs, arow >= 0);
       }
     }
 
@@ -1383,6 +1383,8 @@ static hipError_t launch_stage(int wfmt, int afmt, int bm, const GemmParams& p, 
   if (wfmt == kWMxfp4 && afmt == kAMxfp4) return launch_bm<STAGE, kWMxfp4, kAMxfp4>(bm, p, stream);
   if (wfmt == kWFp8Block && afmt == kAFp8G128) return launch_bm<STAGE, kWFp8Block, kAFp8G128>(bm, p, stream);
   if (wfmt == kWFp8Channel && afmt == kAFp8Token) return launch_bm<STAGE, kWFp8Channel, kAFp8Token>(bm, p, stream);
+  // per tensor: the per-channel kernels with scale strides 0 (GemmParams::wsc_rs, asc_rs)
+  if (wfmt == kWFp8Tensor && afmt == kAFp8Tensor) return launch_bm<STAGE, kWFp8Channel, kAFp8Token>(bm, p, stream);
   return hipErrorInvalidValue;
 }
 

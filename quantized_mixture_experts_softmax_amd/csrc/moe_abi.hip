@@ -44,19 +44,21 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // bytes of codes / scales of a [rows, cols] matrix in activation format f
 size_t code_bytes(int f, size_t rows, size_t cols) {
   if (f == MOE_A_MXFP4_G32) return rows * cols / 2;
-  if (f == MOE_A_FP8_G128 || f == MOE_A_FP8_TOKEN) return rows * cols;
+  if (f == MOE_A_FP8_G128 || f == MOE_A_FP8_TOKEN || f == MOE_A_FP8_TENSOR) return rows * cols;
   return 0;
 }
 size_t scale_bytes(int f, size_t rows, size_t cols) {
   if (f == MOE_A_MXFP4_G32) return rows * (cols / 32);
   if (f == MOE_A_FP8_G128) return rows * ((cols + 127) / 128) * 4;
   if (f == MOE_A_FP8_TOKEN) return rows * 4;
+  if (f == MOE_A_FP8_TENSOR) return 4;
   return 0;
 }
 
 bool pair_supported(int wf, int af) {
   return (wf == MOE_W_MXFP4 && (af == MOE_A_BF16 || af == MOE_A_MXFP4_G32)) ||
-         (wf == MOE_W_FP8_BLOCK128 && af == MOE_A_FP8_G128) || (wf == MOE_W_FP8_CHANNEL && af == MOE_A_FP8_TOKEN);
+         (wf == MOE_W_FP8_BLOCK128 && af == MOE_A_FP8_G128) || (wf == MOE_W_FP8_CHANNEL && af == MOE_A_FP8_TOKEN) ||
+         (wf == MOE_W_FP8_TENSOR && af == MOE_A_FP8_TENSOR);
 }
 
 moe_status check_shapes(const moe_forward_args* a) {
@@ -79,8 +81,8 @@ moe_status check_shapes(const moe_forward_args* a) {
     return fail(MOE_EINVAL, "the router weight goes on the input only with one slot per token (K = %d)", a->K);
   if (a->gate_up_interleaved && a->wfmt == MOE_W_FP8_BLOCK128)
     return fail(MOE_EUNSUPPORTED, "interleaved gate/up rows would split FP8 128x128 scale blocks");
-  if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
-  if (a->afmt < MOE_A_BF16 || a->afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)a->afmt);
+  if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_TENSOR) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
+  if (a->afmt < MOE_A_BF16 || a->afmt > MOE_A_FP8_TENSOR) return fail(MOE_EINVAL, "unknown activation format %d", (int)a->afmt);
   if (!pair_supported(a->wfmt, a->afmt))
     return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)a->wfmt,
                 (int)a->afmt);
@@ -110,13 +112,13 @@ size_t moe_tiled_weight_bytes(moe_wfmt wfmt, int E, int N, int K) {
   if (E < 0 || N < 0 || K < 0 || N % 16 || K % 32) return 0;
   const size_t blocks = (size_t)E * (N / 16) * ((K + 127) / 128);
   if (wfmt == MOE_W_MXFP4) return blocks * 1088;
-  if (wfmt == MOE_W_FP8_BLOCK128 || wfmt == MOE_W_FP8_CHANNEL) return blocks * 2048;
+  if (wfmt == MOE_W_FP8_BLOCK128 || wfmt == MOE_W_FP8_CHANNEL || wfmt == MOE_W_FP8_TENSOR) return blocks * 2048;
   return 0;
 }
 
 moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w, const void* w_scale, uint8_t* out,
                             hipStream_t stream) {
-  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "moe_tile_weights: unknown weight format %d", (int)wfmt);
+  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_TENSOR) return fail(MOE_EINVAL, "moe_tile_weights: unknown weight format %d", (int)wfmt);
   if (E < 0 || N <= 0 || K <= 0 || N % 16 || K % 32 || K > 65536)
     return fail(MOE_EINVAL, "moe_tile_weights: need N %% 16 == 0, K %% 32 == 0, K <= 65536 (got N=%d, K=%d)", N, K);
   if (E > 0 && (!w || !out || (wfmt == MOE_W_MXFP4 && !w_scale))) return fail(MOE_EINVAL, "moe_tile_weights: NULL pointer");
@@ -127,8 +129,8 @@ moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w
 moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I) {
   if (act != MOE_ACT_SILU && act != MOE_ACT_SWIGLU_OAI)
     return fail(MOE_EUNSUPPORTED, "activation %d is not implemented (SiLU-and-mul, SwiGLU-OAI)", (int)act);
-  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_CHANNEL) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
-  if (afmt < MOE_A_BF16 || afmt > MOE_A_FP8_TOKEN) return fail(MOE_EINVAL, "unknown activation format %d", (int)afmt);
+  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_TENSOR) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
+  if (afmt < MOE_A_BF16 || afmt > MOE_A_FP8_TENSOR) return fail(MOE_EINVAL, "unknown activation format %d", (int)afmt);
   if (!pair_supported(wfmt, afmt))
     return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)wfmt, (int)afmt);
   if (H <= 0 || H % 32 || I <= 0 || I % 32 || H > 65536 || I > 65536)
@@ -253,11 +255,13 @@ moe_status moe_route_align(const float* router_logits, int T, int E, int topk, m
 
 moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt, uint8_t* codes, void* scales,
                          hipStream_t stream) {
-  if (fmt != MOE_A_MXFP4_G32 && fmt != MOE_A_FP8_G128 && fmt != MOE_A_FP8_TOKEN)
+  if (fmt != MOE_A_MXFP4_G32 && fmt != MOE_A_FP8_G128 && fmt != MOE_A_FP8_TOKEN && fmt != MOE_A_FP8_TENSOR)
     return fail(MOE_EINVAL, "moe_quant_act: format %d has no quantiser", (int)fmt);
   if (rows < 0) return fail(MOE_EINVAL, "moe_quant_act: rows must be >= 0 (got %d)", rows);
   if (cols <= 0 || cols % 32 || cols > 65536) return fail(MOE_EINVAL, "moe_quant_act: cols must be a positive multiple of 32 <= 65536 (got %d)", cols);
   if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_EINVAL, "moe_quant_act: NULL pointer");
+  if (fmt == MOE_A_FP8_TENSOR && (long long)rows * cols >= 0x7FFFFFFFLL)
+    return fail(MOE_EINVAL, "moe_quant_act: per-tensor quantisation needs rows * cols < 2^31");
   if (!aligned(x, 4) || !aligned(codes, 2) || !aligned(scales, 4)) return fail(MOE_EINVAL, "moe_quant_act: misaligned pointer");
   return hip_status(moe::launch_quant_act(x, rows, cols, (int)fmt, nullptr, codes, scales, stream), "moe_quant_act launch");
 }
@@ -363,6 +367,9 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.interleaved = a->gate_up_interleaved;
   p.bias = a->w1_bias;
   p.weight_on_input = a->apply_router_weight_on_input;
+  p.wsc_es = a->wfmt == MOE_W_FP8_TENSOR ? 1 : p.Nw;  // FP8 weight scales: per tensor or per channel
+  p.wsc_rs = a->wfmt == MOE_W_FP8_TENSOR ? 0 : 1;
+  p.asc_rs = a->afmt == MOE_A_FP8_TENSOR ? 0 : 1;
   if ((e = prof_mark(0, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
   e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
@@ -394,6 +401,7 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.interleaved = 0;
   p.bias = a->w2_bias;
   p.weight_on_input = 0;
+  p.wsc_es = a->wfmt == MOE_W_FP8_TENSOR ? 1 : p.Nw;
   e = moe::launch_gemm(2, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 2");
   if ((e = prof_mark(2, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");

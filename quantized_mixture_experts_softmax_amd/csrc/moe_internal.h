@@ -6,9 +6,12 @@
 namespace moe {
 
 // Activation formats (values match moe_afmt in include/moe.h).
-enum { kABf16 = 0, kAMxfp4 = 1, kAFp8G128 = 2, kAFp8Token = 3 };
-// Weight formats (values match moe_wfmt).
-enum { kWMxfp4 = 0, kWFp8Block = 1, kWFp8Channel = 2 };
+// kAFp8Tensor is quantised by its own kernels; the GEMMs read it as kAFp8Token with a
+// row stride of 0 in the scale array.
+enum { kABf16 = 0, kAMxfp4 = 1, kAFp8G128 = 2, kAFp8Token = 3, kAFp8Tensor = 4 };
+// Weight formats (values match moe_wfmt).  kWFp8Tensor runs as kWFp8Channel with scale
+// strides (expert 1, row 0).
+enum { kWMxfp4 = 0, kWFp8Block = 1, kWFp8Channel = 2, kWFp8Tensor = 3 };
 
 // One grouped-GEMM launch over the padded sorted rows.
 struct GemmParams {
@@ -41,7 +44,15 @@ struct GemmParams {
   int interleaved;     // stage 1: w13 rows alternate gate_n, up_n (else gate rows, then up rows)
   const uint16_t* bias;
   int weight_on_input;  // stage 1: the slot's top-k weight scales both projections (top-1)
+  // FP8 channel-path scale strides: weight scale of (expert e, row n) at e * wsc_es + n *
+  // wsc_rs (per channel: Nw, 1; per tensor: 1, 0); activation scale of row r at r * asc_rs
+  // (per token 1, per tensor 0).
+  int wsc_es, wsc_rs, asc_rs;
 };
+
+__device__ __forceinline__ size_t wsc_index(const GemmParams& p, int e, int row) {
+  return (size_t)e * p.wsc_es + (size_t)row * p.wsc_rs;
+}
 
 constexpr int kActSilu = 0, kActSwigluOai = 1;
 

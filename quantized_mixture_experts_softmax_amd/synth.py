@@ -81,6 +81,9 @@ WORKLOADS = {
                           score=SCORE_SIGMOID, n_shared=1, shared_weight=1.0, seed=1003),
     "fp8-channel": Workload("fp8-channel", 4096, 4096, 14336, 8, 2, W_FP8_CHANNEL, A_FP8_TOKEN, seed=1004,
                             T_sweep=(1, 16, 256, 4096)),
+    # per-tensor FP8 leaf at the fp8-channel shapes (not a configuration of its own)
+    "fp8-tensor": Workload("fp8-tensor", 4096, 4096, 14336, 8, 2, W_FP8_TENSOR, A_FP8_TENSOR, seed=1005,
+                           T_sweep=(1, 16, 256, 4096)),
 }
 
 _FP8_MAG_MASK = np.uint64(0xBFBFBFBFBFBFBFBF)  # clear exponent bit 3 (bit 6 of the byte)

@@ -326,3 +326,19 @@ def test_full_size_fp8_channel_sweep(fp8_channel_data, T):
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
     full_check(w, data, res, tokens=_sample(T, 6, 8), what=f"{w.name}/T{T}")
+
+
+FP8T = (synth.W_FP8_TENSOR, synth.A_FP8_TENSOR)
+FP8T_CASES = [(bm, tiled) for bm in (16, 32, 64, 128) for tiled in (False, True)]
+
+
+@pytest.mark.parametrize("bm,tiled", FP8T_CASES, ids=[f"bm{bm}-{'tiled' if t else 'canon'}" for bm, t in FP8T_CASES])
+def test_fp8_per_tensor(bm, tiled):
+    """Per-tensor FP8 (one weight scale per expert and projection, one dynamic activation
+    scale per tensor) on every kernel; the whole batch is checked (the scales depend on it)."""
+    w = small(FP8T, T=33, H=320, I=416, E=4, k=2)
+    data = synth.make_all(w)
+    say(f"forward fp8-tensor bm={bm} tiled={tiled}")
+    res = run_layer(w, data, block_m=bm, tiled=tiled)
+    assert res["a1_scales"].view(np.float32).size == 1
+    full_check(w, data, res, what=f"fp8-tensor/bm{bm}/{'tiled' if tiled else 'canon'}")

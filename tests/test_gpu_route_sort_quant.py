@@ -123,7 +123,9 @@ def test_align_sort_invalid_ids_dropped():
 
 QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8_G128, 33, 160),
                ("fp8-token", B.A_FP8_TOKEN, 40, 4096), ("fp8-token-wide", B.A_FP8_TOKEN, 3, 14336),
-               ("mxfp4", B.A_MXFP4_G32, 40, 2880), ("mxfp4-small", B.A_MXFP4_G32, 1, 32)]
+               ("mxfp4", B.A_MXFP4_G32, 40, 2880), ("mxfp4-small", B.A_MXFP4_G32, 1, 32),
+               ("fp8-tensor", B.A_FP8_TENSOR, 40, 4096), ("fp8-tensor-big", B.A_FP8_TENSOR, 4096, 7168),
+               ("fp8-tensor-one", B.A_FP8_TENSOR, 1, 32)]
 
 
 @pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
