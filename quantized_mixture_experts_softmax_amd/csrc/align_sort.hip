@@ -13,12 +13,10 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "route_device.h"
+#include "sort_device.h"
 
 namespace moe {
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kSortChunk = 4096;
 constexpr int kMaxExperts = 1024;
 
 // Lanes of this wave whose key equals mine (key < 2048).
@@ -30,56 +28,6 @@ __device__ __forceinline__ uint64_t match_key(int key) {
     m &= ((key >> b) & 1) ? bal : ~bal;
   }
   return m;
-}
-
-// Block-wide exclusive scan of one value per thread (kSortThreads threads).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
-  const int lane = lane_id(), w = (int)threadIdx.x / kWave;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
-  }
-  if (lane == kWave - 1) wsum[w] = inc;
-  __syncthreads();
-  if (w == 0) {
-    int x = lane < kSortWaves ? wsum[lane] : 0;
-    int xi = x;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int n = __shfl_up(xi, o, kWave);
-      if (lane >= o) xi += n;
-    }
-    if (lane < kSortWaves) wsum[lane] = xi - x;  // exclusive wave base
-    if (lane == kSortWaves - 1) *total = xi;
-  }
-  __syncthreads();
-  return wsum[w] + inc - v;
-}
-
-// Rows p = start, start + stride, ... < cap: pad rows (past an expert's count inside its
-// padded run, or past the total) get the sentinel n; the first row of every block gets
-// the block's owner (-1 past the total).  offs [E + 1] and cnt [E] are the padded
-// offsets and counts.
-__device__ __forceinline__ void fill_pads_owners(const int* offs, const int* cnt, int E, int total, int n, int bm,
-                                                 int cap, int start, int stride, int32_t* __restrict__ sorted,
-                                                 int32_t* __restrict__ block_expert) {
-  for (int p = start; p < cap; p += stride) {
-    bool pad = p >= total;
-    if (!pad) {
-      int lo = 0, hi = E - 1;  // last e with offs[e] <= p
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= p) lo = mid; else hi = mid - 1;
-      }
-      pad = p >= offs[lo] + cnt[lo];
-      if ((p % bm) == 0) block_expert[p / bm] = lo;
-    } else if ((p % bm) == 0 && p / bm < cap / bm) {
-      block_expert[p / bm] = -1;
-    }
-    if (pad) sorted[p] = n;
-  }
 }
 
 // The sort as run by workgroup `chunk` of `nchunks` (kSortThreads threads).  `ids` may
@@ -168,107 +116,17 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
                   num_padded);
 }
 
-// Router + sort in one workgroup (route_sort_fusable: E <= 64, small batch).  The
-// logits are staged in LDS (row stride E + 1, so the lanes of a wave, which hold
-// different tokens, hit different banks).  Waves take (expert e, group of 64 tokens)
-// tasks: lane t counts the experts ranking before e in its token (an expert j < e
-// ranks before on >=, j > e on >, the id tie rule), the lanes of rank < k are the
-// token's winners, and the wave's ballot of them is the 64-token selection mask of e.
-// Because an expert is chosen at most once per token, the stable position of slot
-// (t, j) inside expert e is the number of earlier tokens choosing e: the masks' popcount
-// prefix over token groups plus the popcount of the lower lanes.  Shared experts are
-// chosen by every token, at position t.  Ids, weights and the sort equal those of the
-// separate router and align-sort kernels.
-constexpr int kFuseLogits = 8192;  // T * E limit of the fused kernel
-constexpr int kFuseMasks = 192;    // >= E * ceil(T / 64) when T * E <= kFuseLogits, E <= 64
-
+// Router + sort in one workgroup (route_sort_fusable: E <= 64, small batch): the body is
+// route_sort_block (sort_device.h).  The logits are staged in LDS with row stride E + 1,
+// so the lanes of a wave, which hold different tokens, hit different banks.
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const float* __restrict__ logits, int T, int E, int topk, int score, int renorm, int n_shared, float shared_w,
     int bm, int cap, int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ counts_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  __shared__ float lg[kFuseLogits + kSortChunk];  // [T][E + 1]; T <= kSortChunk
-  __shared__ float sel_v[kSortChunk];             // [T][topk] winning logits by rank
-  __shared__ int sel_e[kSortChunk];               // [T][topk] winning experts by rank
-  __shared__ unsigned long long mask[kFuseMasks]; // [E][G] selection masks
-  __shared__ int pre[kFuseMasks];                 // [E][G] selections in earlier groups
-  __shared__ int cnt[kSmallE + 32];
-  __shared__ int offs[kSmallE + 32 + 1];
-  __shared__ int wsum[kSortWaves];
-  __shared__ int grand_total;
-  const int tid = (int)threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int KP = topk + n_shared, Et = E + n_shared, n = T * KP, G = (T + kWave - 1) / kWave, ld = E + 1;
-
-  for (int i = tid; i < T * E; i += kSortThreads) {
-    const int t = i / E;
-    lg[t * ld + (i - t * E)] = logits[i];
-  }
-  __syncthreads();
-  for (int task = w; task < E * G; task += kSortWaves) {  // wave-uniform
-    const int e = task / G, g = task - e * G, t = g * kWave + lane;
-    const bool ok = t < T;
-    const float* row = lg + (ok ? t : 0) * ld;
-    const float v = row[e];
-    int rank = 0;
-    for (int j = 0; j < e; ++j) rank += row[j] >= v ? 1 : 0;
-    for (int j = e + 1; j < E; ++j) rank += row[j] > v ? 1 : 0;
-    const bool sel = ok && rank < topk;
-    const unsigned long long m = __ballot(sel);
-    if (lane == 0) mask[task] = m;
-    if (sel) {
-      sel_e[t * topk + rank] = e;
-      sel_v[t * topk + rank] = v;
-    }
-  }
-  __syncthreads();
-  // per-expert counts (shared experts: every token) and group prefixes
-  if (tid < Et) {
-    int c = T;
-    if (tid < E) {
-      c = 0;
-      for (int g = 0; g < G; ++g) {
-        pre[tid * G + g] = c;
-        c += __popcll(mask[tid * G + g]);
-      }
-    }
-    cnt[tid] = c;
-  }
-  __syncthreads();
-  const int padded = tid < Et ? (cnt[tid] + bm - 1) / bm * bm : 0;
-  const int off = block_exclusive_scan(padded, wsum, &grand_total);
-  if (tid < Et) offs[tid] = off;
-  if (tid == 0) offs[Et] = grand_total;
-  __syncthreads();
-  const int total = grand_total;
-  if (tid < Et) {
-    counts_out[tid] = cnt[tid];
-    offsets_out[tid] = offs[tid];
-  }
-  if (tid == 0) {
-    offsets_out[Et] = total;
-    num_padded[0] = total;
-  }
-  // slots: ids, weights and their sorted rows
-  for (int q = tid; q < n; q += kSortThreads) {
-    const int t = q / KP, j = q - t * KP;
-    int e, pos;
-    float wt;
-    if (j < topk) {
-      e = sel_e[t * topk + j];
-      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, lg + t * ld, E);
-      const int g = t / kWave, l = t % kWave;
-      const unsigned long long below = l ? (~0ull >> (kWave - l)) : 0ull;
-      pos = offs[e] + pre[e * G + g] + __popcll(mask[e * G + g] & below);
-    } else {
-      e = E + (j - topk);
-      wt = shared_w;
-      pos = offs[e] + t;
-    }
-    ids[q] = e;
-    weights[q] = wt;
-    sorted[pos] = q;
-  }
-  fill_pads_owners(offs, cnt, Et, total, n, bm, cap, tid, kSortThreads, sorted, block_expert);
+  __shared__ __attribute__((aligned(16))) uint8_t scratch[kRouteSortLdsMax];
+  RouteSortOut o{ids, weights, counts_out, offsets_out, sorted, block_expert, num_padded};
+  route_sort_block(logits, T, E, topk, score, renorm, n_shared, shared_w, bm, cap, scratch, o);
 }
 
 bool route_sort_fusable(int T, int E, int K) {
