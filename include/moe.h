@@ -305,6 +305,27 @@ moe_status moe_workspace_layout(const moe_forward_args* a, moe_workspace_layout_
 moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_layer_forward -- the whole layer from router logits: moe_route_align (E = E_total -
+ * n_shared routed experts, topk = K - n_shared, the block_m of `a`) writing into the
+ * routing buffers that `a` names, then moe_experts_forward(a).  The pages' layer takes
+ * router_logits and performs the top-k selection before the expert kernels
+ * ([rocm_aiter_moe] rocm_aiter_fused_experts; [mxfp4.py] Mxfp4MoEMethod.apply_monolithic).
+ *   router_logits   [T, E] fp32
+ *   a->topk_ids, a->topk_weights, a->sorted_slots, a->block_expert, a->num_padded
+ *                   OUTPUTS here (layouts of moe_route_align / moe_align_sort), despite
+ *                   the const in the struct, which describes moe_experts_forward
+ *   expert_counts [E_total], expert_offsets [E_total + 1]: outputs as moe_align_sort
+ * Every output equals that of the two separate calls bit for bit.  For a batch with
+ * block_m == 16, E <= 64, T*K <= 4096, T*E <= 8192 and the stage-1 LDS budget met (no
+ * apply_router_weight_on_input) the stage-1 kernel routes and sorts the batch itself,
+ * saving a launch; otherwise the separate launches run.  Limits: those of the two calls,
+ * 0 <= n_shared < K.  Device pointers; enqueued on `stream`.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_layer_forward(const moe_forward_args* a, const float* router_logits, moe_score score,
+                             int renormalize, int n_shared, float shared_weight, int32_t* expert_counts,
+                             int32_t* expert_offsets, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_tile_weights -- one-time permutation of one weight tensor ([E, N, K] codes in the
  * canonical layout of `wfmt`, i.e. w1 with N = 2I, K = H or w2 with N = H, K = I) into
  * MOE_LAYOUT_TILED.  Block (e, n16, c) holds rows [16*n16, 16*n16+16) and K elements

@@ -22,7 +22,7 @@ ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
 EXPORTED = [
     "moe_route_topk", "moe_route_grouped_topk", "moe_map_experts", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
-    "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward",
+    "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward", "moe_layer_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
     "moe_tiled_weight_bytes", "moe_tile_weights",
 ]
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.POINTER(WorkspaceLayout)]
         L.moe_experts_forward.restype = S
         L.moe_experts_forward.argtypes = [ctypes.POINTER(ForwardArgs), P]
+        L.moe_layer_forward.restype = S
+        L.moe_layer_forward.argtypes = [ctypes.POINTER(ForwardArgs), P, I, I, I, ctypes.c_float, P, P, P]
         L.moe_supports.restype = S
         L.moe_supports.argtypes = [I, I, I, I, I]
         L.moe_pick_block_m.restype = I
@@ -367,22 +369,53 @@ def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, top
     return out, workspace
 
 
+def moe_layer_forward(hidden_states, router_logits, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict,
+                      wfmt: int, afmt: int, block_m: int, E_total: int, I: int, score: str = "softmax",
+                      renormalize: bool = True, n_shared: int = 0, shared_weight: float = 1.0, out=None,
+                      workspace=None, a1_codes=None, a1_scales=None, stream=None,
+                      weight_layout: int = LAYOUT_CANONICAL, act: dict | None = None):
+    """Route + align-sort into topk_ids, topk_weights and sort (the moe_align_sort dict),
+    then the expert layer, in one call; small batches are routed inside stage 1.
+    Returns (out, workspace)."""
+    dev = _dev(hidden_states)
+    assert hidden_states.dtype == torch.bfloat16
+    assert router_logits.dtype == torch.float32 and router_logits.dim() == 2
+    T, H = hidden_states.shape
+    assert router_logits.shape == (T, E_total - n_shared)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    args = forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort, wfmt, afmt,
+                        block_m, E_total, I, out, workspace, a1_codes, a1_scales, weight_layout, act)
+    need = moe_experts_workspace_bytes(args)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(lib().moe_layer_forward(ctypes.byref(args), _ptr(router_logits), SCORE[score], int(renormalize), n_shared,
+                                   shared_weight, _ptr(sort["expert_counts"]), _ptr(sort["expert_offsets"]),
+                                   _stream(stream, dev)))
+    return out, workspace
+
+
 class MoELayer:
     """Device-resident weights of one quantised MoE expert layer and the full hot
-    path: route + align-sort (one moe_route_align call), optional a1 quantisation,
-    experts forward.  Buffers are allocated on first use and reused."""
+    path: route + align-sort, optional a1 quantisation, experts forward (one
+    moe_layer_forward call, or moe_route_align + moe_experts_forward with
+    fuse_route=False).  Buffers are allocated on first use and reused."""
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
                  tiled: bool = False, grouped: dict | None = None, act: dict | None = None,
-                 expert_map: torch.Tensor | None = None):
+                 expert_map: torch.Tensor | None = None, fuse_route: bool = True):
         """tiled=True re-lays the weights once into the kernel layout (moe_tile_weights).
         grouped = dict(num_expert_group, topk_group, correction_bias (tensor or None),
         routed_scaling_factor) routes with moe_route_grouped_topk (then moe_align_sort).
         act: activation, row order and biases, as for forward_args (None: SiLU-and-mul).
         expert_map (int32 [E + n_shared] global -> local id or -1): this device's share of an
         expert-parallel layer; the weights hold the local experts only, the router runs over
-        the global experts and moe_map_experts turns its ids into local ones."""
+        the global experts and moe_map_experts turns its ids into local ones.
+        fuse_route: plain top-k routing goes through moe_layer_forward (routing inside
+        stage 1 where the batch allows); False keeps the separate calls."""
         self.E_local = w1.shape[0]
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
@@ -400,6 +433,7 @@ class MoELayer:
         self.grouped = grouped
         self.act = act
         self.expert_map = expert_map
+        self.fuse_route = fuse_route
         if expert_map is None:
             assert self.E_local == self.E_total, "weights hold E + n_shared experts (or pass expert_map)"
         self._bufs: dict = {}
@@ -432,6 +466,15 @@ class MoELayer:
     def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
         T = x.shape[0]
         b = self._buffers(T, x.device)
+        if self.fuse_route and self.expert_map is None and self.grouped is None:
+            a1c = a1s = None
+            if self.afmt != A_BF16:
+                a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
+            out, b["workspace"] = moe_layer_forward(
+                x, router_logits, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"],
+                self.wfmt, self.afmt, b["bm"], self.E_local, self.I, self.score, True, self.n_shared,
+                self.shared_weight, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
+            return out
         if self.expert_map is not None:
             moe_route_topk(router_logits, self.topk, self.score, True, self.n_shared, self.shared_weight,
                            b["ids_global"], b["w"], stream)

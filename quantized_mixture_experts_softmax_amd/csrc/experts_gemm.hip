@@ -33,6 +33,7 @@
 // share the expert's weight strip in that XCD's L2.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "sort_device.h"
 
 #include <algorithm>
 
@@ -903,7 +904,15 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
 // tile is XOR-swizzled: 16-byte unit u of row r sits at unit u ^ (r mod units per
 // chunk), so the fragment reads of the 16 rows spread over the LDS banks although each
 // direct load writes 1 KB contiguously.
-template <int STAGE, int WF, int AF, int D, int WAVES, int WL, int EPI>
+//
+// RS = 1 (stage 1 only): the router and the align-sort run inside the kernel.  Every
+// workgroup routes and sorts the whole batch in LDS (route_sort_block, its scratch
+// overlapping the tile region) before its first phase, keeps the sorted rows, block
+// owners and padded total in an LDS region of their own, and takes its tables from
+// there; workgroup 0 also writes ids, weights, counts, offsets and the tables to global
+// memory for stage 2 and the combine.  The tables are the same integers the separate
+// router + sort kernels produce, so the result does not change.
+template <int STAGE, int WF, int AF, int D, int WAVES, int WL, int EPI, int RS>
 __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const GemmParams p) {
   using WLay = WLayout<WF, WL>;
   constexpr int BM = 16, NT = 2;
@@ -920,7 +929,29 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps run bookkeeping scalar
   const int K = p.K, nch = (K + 127) / 128;
   const int U = (STAGE == 1) ? (p.N + 15) / 16 : (p.N + 31) / 32;  // units per block
-  const int nb = min(p.num_padded[0] / BM, p.num_blocks);          // blocks in use
+  int npad;
+  int32_t *rs_sorted = nullptr, *rs_owner = nullptr;  // RS: the tables in LDS
+  if constexpr (RS) {
+    static_assert(STAGE == 1 && 64 * WAVES == kSortThreads, "the fused route + sort runs in stage 1 with 1024 threads");
+    rs_sorted = (int32_t*)(smem + p.route_keep_off);
+    rs_owner = rs_sorted + p.route_cap;
+    int32_t* rs_total = rs_owner + p.route_cap / BM;
+    const bool first = blockIdx.x == 0;
+    const RouteSortOut o{first ? p.out_ids : nullptr, first ? p.out_weights : nullptr,
+                         first ? p.out_counts : nullptr, first ? p.out_offsets : nullptr, rs_sorted, rs_owner, rs_total};
+    route_sort_block(p.logits, p.T, p.route_E, p.route_topk, p.route_score, p.route_renorm, p.route_n_shared,
+                     p.route_shared_w, BM, p.route_cap, smem, o);
+    __syncthreads();
+    npad = *rs_total;
+    if (first) {
+      for (int i = (int)threadIdx.x; i < p.route_cap; i += kThreads) p.out_sorted[i] = rs_sorted[i];
+      for (int i = (int)threadIdx.x; i < p.route_cap / BM; i += kThreads) p.out_block_expert[i] = rs_owner[i];
+      if (threadIdx.x == 0) p.out_num_padded[0] = npad;
+    }
+  } else {
+    npad = p.num_padded[0];
+  }
+  const int nb = min(npad / BM, p.num_blocks);  // blocks in use
   const long L = (long)nb * U;
   const int P = (int)gridDim.x;
   const int wg = xcd_remap((int)blockIdx.x, P);  // neighbouring ranges (same block) share an XCD
@@ -946,7 +977,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     const int ua = (int)(u_next - (long)b * U);
     const int ub = (int)min((long)U, r_end - (long)b * U);
     u_next = (long)b * U + ub;
-    const int e = p.block_expert[b];
+    const int e = RS ? rs_owner[b] : p.block_expert[b];
     if (e < 0) continue;  // workgroup-uniform
 
     const int S = (ub - ua) * nch;  // steps of the phase
@@ -995,7 +1026,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     lds_barrier();
     int slot_v = 0;
     if (tid < BM) {
-      slot_v = p.sorted_slots[b * BM + tid];
+      slot_v = RS ? rs_sorted[b * BM + tid] : p.sorted_slots[b * BM + tid];
       if (STAGE == 1) lds_row[tid] = slot_v < TK ? slot_v / p.slots_per_token : -1;
     }
     if (STAGE == 1) lds_barrier();
@@ -1256,15 +1287,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (idx >= (long)T * per_row) return;
   const int t = (int)(idx / per_row), c = (int)(idx % per_row) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < K; ++j) {
-    const int e = ids[(size_t)t * K + j];
-    if (e < 0 || e >= E) continue;
-    const float w = wts ? wts[(size_t)t * K + j] : 1.0f;
-    const f32x4 y = *(const f32x4*)(ybuf + ((size_t)t * K + j) * H + c);
+  // four slots at a time: their ids and weights, then their rows, are loaded together
+  // (indices clamped to the token's last slot; a row of a skipped slot is read, not used)
+  constexpr int kGroup = 4;
+  for (int j0 = 0; j0 < K; j0 += kGroup) {
+    int e[kGroup];
+    float w[kGroup];
+    f32x4 y[kGroup];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float prod = y[i] * w;
-      acc[i] = acc[i] + prod;
+    for (int q = 0; q < kGroup; ++q) {
+      const int j = min(j0 + q, K - 1);
+      e[q] = ids[(size_t)t * K + j];
+      w[q] = wts ? wts[(size_t)t * K + j] : 1.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      const int j = min(j0 + q, K - 1);
+      y[q] = *(const f32x4*)(ybuf + ((size_t)t * K + j) * H + c);
+    }
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      if (j0 + q >= K || e[q] < 0 || e[q] >= E) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float prod = y[q][i] * w[q];
+        acc[i] = acc[i] + prod;
+      }
     }
   }
   const uint32_t lo = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
@@ -1272,7 +1320,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *(uint2*)(out + (size_t)t * H + c) = make_uint2(lo, hi);
 }
 
-constexpr size_t kPersistLdsMax = 128 * 1024;  // dynamic LDS the persistent kernel may use
+// Dynamic LDS of the persistent kernel: up to kPersistLdsMax it serves 16-row blocks
+// (larger activation tiles go to the K-split kernel); with the route + sort fused in it
+// may take up to a CU's whole LDS, kPersistLdsFusedMax.
+constexpr size_t kPersistLdsMax = 128 * 1024;
+constexpr size_t kPersistLdsFusedMax = 160 * 1024;
 #ifndef MOE_PERSIST_WAVES
 #define MOE_PERSIST_WAVES 16
 #endif
@@ -1303,15 +1355,53 @@ static size_t persist_lds_bytes(int afmt, int K, int waves) {
   return tile16_lds_bytes(afmt, K) + (size_t)waves * 2 * 4 * 64 * 4;
 }
 
-template <int STAGE, int WF, int AF, int WL, int EPI>
+// Dynamic LDS a persistent workgroup may take on the current device: kPersistLdsFusedMax,
+// or less where the device's per-workgroup limit is lower.
+static size_t persist_lds_limit() {
+  static int lim[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+  if (lim[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0)
+      n = 64 * 1024;
+    lim[dev] = n;
+  }
+  return std::min((size_t)lim[dev], kPersistLdsFusedMax);
+}
+
+// LDS of the persistent stage-1 kernel with the route + sort fused in: the route
+// scratch overlaps the tile and partial-sum region; the kept tables (sorted rows [cap],
+// block owners [cap / 16], padded total) follow both.  False when the batch is too
+// large for the one-workgroup route + sort or the LDS does not fit.
+static bool route_stage1_lds(int afmt, int K_dim, int T, int E, int topk, int n_shared, size_t* keep_off,
+                             size_t* total) {
+  if (64 * MOE_PERSIST_WAVES != kSortThreads || !route_sort_fusable(T, E, topk + n_shared)) return false;
+  const long cap = (long)T * (topk + n_shared) + (long)(E + n_shared) * 15;
+  const size_t base = persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES);
+  const size_t scratch = route_sort_lds_bytes(T, E, topk, n_shared, (T + kWave - 1) / kWave);
+  const size_t off = (std::max(base, scratch) + 15) / 16 * 16;
+  const size_t all = off + (size_t)(cap + cap / 16 + 1) * 4;
+  *keep_off = off;
+  *total = all;
+  return all <= persist_lds_limit();
+}
+
+bool route_stage1_fusable(int afmt, int K_dim, int T, int E, int topk, int n_shared) {
+  size_t off = 0, all = 0;
+  return T > 0 && route_stage1_lds(afmt, K_dim, T, E, topk, n_shared, &off, &all);
+}
+
+template <int STAGE, int WF, int AF, int WL, int EPI, int RS>
 static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t stream) {
   constexpr int WAVES = MOE_PERSIST_WAVES;
   constexpr int D = (WF == kWMxfp4) ? MOE_PERSIST_DEPTH_F4 : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
   if (p.num_blocks == 0) return hipSuccess;
-  auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI>;
+  auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI, RS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPersistLdsMax);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)persist_lds_limit());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1329,9 +1419,21 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
 template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
+    if constexpr (STAGE == 1 && 64 * MOE_PERSIST_WAVES == kSortThreads) {
+      if (p_in.route) {
+        GemmParams p = p_in;
+        size_t keep_off = 0, lds = 0;
+        if (!route_stage1_lds(AF, p.K, p.T, p.route_E, p.route_topk, p.route_n_shared, &keep_off, &lds))
+          return hipErrorInvalidValue;
+        p.route_keep_off = (int)keep_off;
+        return launch_persist<STAGE, WF, AF, WL, EPI, 1>(p, lds, stream);
+      }
+    }
     const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
-    if (lds <= kPersistLdsMax) return launch_persist<STAGE, WF, AF, WL, EPI>(p_in, lds, stream);
+    if (lds <= std::min(kPersistLdsMax, persist_lds_limit()))
+      return launch_persist<STAGE, WF, AF, WL, EPI, 0>(p_in, lds, stream);
   }
+  if (p_in.route) return hipErrorInvalidValue;  // the fused route + sort runs in the persistent kernel only
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;
   constexpr int COLS_PER_WG = kSplit ? ((STAGE == 1) ? 8 * NT : 16 * NT) : ((STAGE == 1) ? 32 * NT : 64 * NT);

@@ -221,24 +221,43 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int K, int E_total, in
                     "moe_align_sort launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+moe_status check_route_align(const char* fn, const float* router_logits, int T, int E, int topk, moe_score score,
+                             int n_shared, int block_m, const int32_t* topk_ids, const float* topk_weights,
+                             const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* sorted_slots,
+                             const int32_t* block_expert, const int32_t* num_padded) {
+  if (T < 0) return fail(MOE_EINVAL, "%s: T must be >= 0 (got %d)", fn, T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "%s: E must be in [1, 1024] (got %d)", fn, E);
+  if (topk < 1 || topk > E || topk > 32) return fail(MOE_EINVAL, "%s: topk must be in [1, min(E, 32)] (got %d)", fn, topk);
+  if (n_shared < 0 || n_shared > 32) return fail(MOE_EINVAL, "%s: n_shared must be in [0, 32] (got %d)", fn, n_shared);
+  if (E + n_shared > 1024) return fail(MOE_EINVAL, "%s: E + n_shared must be <= 1024 (got %d)", fn, E + n_shared);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return fail(MOE_EINVAL, "%s: unknown score %d", fn, (int)score);
+  if (!valid_bm(block_m)) return fail(MOE_EINVAL, "%s: block_m must be 16, 32, 64 or 128 (got %d)", fn, block_m);
+  const int K = topk + n_shared, E_total = E + n_shared;
+  if ((long long)T * K + (long long)E_total * block_m >= 0x7FFFFFFFLL) return fail(MOE_EINVAL, "%s: T*K too large", fn);
+  if (!expert_counts || !expert_offsets || !sorted_slots || !block_expert || !num_padded ||
+      (T > 0 && (!router_logits || !topk_ids || !topk_weights)))
+    return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "%s: pointers must be 4-byte aligned", fn);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_route_align(const float* router_logits, int T, int E, int topk, moe_score score, int renormalize,
                            int n_shared, float shared_weight, int block_m, int32_t* topk_ids, float* topk_weights,
                            int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slots,
                            int32_t* block_expert, int32_t* num_padded, hipStream_t stream) {
-  if (T < 0) return fail(MOE_EINVAL, "moe_route_align: T must be >= 0 (got %d)", T);
-  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "moe_route_align: E must be in [1, 1024] (got %d)", E);
-  if (topk < 1 || topk > E || topk > 32) return fail(MOE_EINVAL, "moe_route_align: topk must be in [1, min(E, 32)] (got %d)", topk);
-  if (n_shared < 0 || n_shared > 32) return fail(MOE_EINVAL, "moe_route_align: n_shared must be in [0, 32] (got %d)", n_shared);
-  if (E + n_shared > 1024) return fail(MOE_EINVAL, "moe_route_align: E + n_shared must be <= 1024 (got %d)", E + n_shared);
-  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return fail(MOE_EINVAL, "moe_route_align: unknown score %d", (int)score);
-  if (!valid_bm(block_m)) return fail(MOE_EINVAL, "moe_route_align: block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+  moe_status st0 = check_route_align("moe_route_align", router_logits, T, E, topk, score, n_shared, block_m, topk_ids,
+                                     topk_weights, expert_counts, expert_offsets, sorted_slots, block_expert, num_padded);
+  if (st0 != MOE_OK) return st0;
   const int K = topk + n_shared, E_total = E + n_shared;
-  if ((long long)T * K + (long long)E_total * block_m >= 0x7FFFFFFFLL) return fail(MOE_EINVAL, "moe_route_align: T*K too large");
-  if (!expert_counts || !expert_offsets || !sorted_slots || !block_expert || !num_padded ||
-      (T > 0 && (!router_logits || !topk_ids || !topk_weights)))
-    return fail(MOE_EINVAL, "moe_route_align: NULL pointer");
-  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
-    return fail(MOE_EINVAL, "moe_route_align: pointers must be 4-byte aligned");
   if (moe::route_sort_fusable(T, E, K))
     return hip_status(moe::launch_route_sort(router_logits, T, E, topk, (int)score, renormalize ? 1 : 0, n_shared,
                                              shared_weight, block_m, topk_ids, topk_weights, expert_counts,
@@ -298,7 +317,19 @@ size_t moe_experts_workspace_bytes(const moe_forward_args* a) {
   return L.total;
 }
 
-moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Routing that stage 1 performs itself (moe_layer_forward on a small batch).
+struct FusedRoute {
+  const float* logits;
+  int E, topk, score, renorm, n_shared;
+  float shared_w;
+  int32_t *counts, *offsets;
+};
+
+moe_status experts_forward(const moe_forward_args* a, const FusedRoute* r, hipStream_t stream) {
   moe_workspace_layout_t L;
   moe_status st = moe_workspace_layout(a, &L);
   if (st != MOE_OK) return st;
@@ -370,10 +401,29 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   p.wsc_es = a->wfmt == MOE_W_FP8_TENSOR ? 1 : p.Nw;  // FP8 weight scales: per tensor or per channel
   p.wsc_rs = a->wfmt == MOE_W_FP8_TENSOR ? 0 : 1;
   p.asc_rs = a->afmt == MOE_A_FP8_TENSOR ? 0 : 1;
+  if (r) {  // stage 1 routes and sorts; its workgroup 0 writes the tables read below
+    p.route = 1;
+    p.logits = r->logits;
+    p.route_E = r->E;
+    p.route_topk = r->topk;
+    p.route_score = r->score;
+    p.route_renorm = r->renorm;
+    p.route_n_shared = r->n_shared;
+    p.route_shared_w = r->shared_w;
+    p.route_cap = (int)cap;
+    p.out_ids = const_cast<int32_t*>(a->topk_ids);
+    p.out_weights = const_cast<float*>(a->topk_weights);
+    p.out_counts = r->counts;
+    p.out_offsets = r->offsets;
+    p.out_sorted = const_cast<int32_t*>(a->sorted_slots);
+    p.out_block_expert = const_cast<int32_t*>(a->block_expert);
+    p.out_num_padded = const_cast<int32_t*>(a->num_padded);
+  }
   if ((e = prof_mark(0, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
   e = moe::launch_gemm(1, (int)a->wfmt, afmt, a->block_m, p, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: stage 1");
   if ((e = prof_mark(1, stream)) != hipSuccess) return hip_status(e, "moe_experts_forward: profiling event");
+  p.route = 0;
 
   // a2: re-quantise h in the activation format
   const void* a2 = h;
@@ -411,6 +461,42 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
                           a->H, a->E_total, a->out, stream);
   if (e != hipSuccess) return hip_status(e, "moe_experts_forward: combine");
   return hip_status(prof_mark(3, stream), "moe_experts_forward: profiling event");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
+  return experts_forward(a, nullptr, stream);
+}
+
+moe_status moe_layer_forward(const moe_forward_args* a, const float* router_logits, moe_score score, int renormalize,
+                             int n_shared, float shared_weight, int32_t* expert_counts, int32_t* expert_offsets,
+                             hipStream_t stream) {
+  moe_status st = check_shapes(a);
+  if (st != MOE_OK) return st;
+  if (n_shared < 0 || n_shared >= a->K || n_shared >= a->E_total)
+    return fail(MOE_EINVAL, "moe_layer_forward: n_shared must be in [0, min(K, E_total)) (got %d)", n_shared);
+  const int E = a->E_total - n_shared, topk = a->K - n_shared;
+  st = check_route_align("moe_layer_forward", router_logits, a->T, E, topk, score, n_shared, a->block_m, a->topk_ids,
+                         a->topk_weights, expert_counts, expert_offsets, a->sorted_slots, a->block_expert,
+                         a->num_padded);
+  if (st != MOE_OK) return st;
+  // stage 1 on the persistent 16-row kernel routes and sorts the batch itself; the
+  // router weight on the input is read by stage 1 and so needs the weights first
+  if (a->block_m == 16 && !a->apply_router_weight_on_input &&
+      moe::route_stage1_fusable((int)a->afmt, a->H, a->T, E, topk, n_shared)) {
+    const FusedRoute r{router_logits, E, topk, (int)score, renormalize ? 1 : 0, n_shared, shared_weight,
+                       expert_counts, expert_offsets};
+    return experts_forward(a, &r, stream);
+  }
+  st = moe_route_align(router_logits, a->T, E, topk, score, renormalize, n_shared, shared_weight, a->block_m,
+                       const_cast<int32_t*>(a->topk_ids), const_cast<float*>(a->topk_weights), expert_counts,
+                       expert_offsets, const_cast<int32_t*>(a->sorted_slots), const_cast<int32_t*>(a->block_expert),
+                       const_cast<int32_t*>(a->num_padded), stream);
+  if (st != MOE_OK) return st;
+  return experts_forward(a, nullptr, stream);
 }
 
 }  // extern "C"

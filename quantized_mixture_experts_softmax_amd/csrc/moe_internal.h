@@ -48,6 +48,17 @@ struct GemmParams {
   // wsc_rs (per channel: Nw, 1; per tensor: 1, 0); activation scale of row r at r * asc_rs
   // (per token 1, per tensor 0).
   int wsc_es, wsc_rs, asc_rs;
+  // Stage 1 with the router + align-sort fused in (the persistent 16-row kernel): every
+  // workgroup routes and sorts the batch in LDS; workgroup 0 writes the results.
+  int route;                 // 0: sorted_slots / block_expert / num_padded are inputs
+  const float* logits;       // [T, route_E] fp32
+  int route_E, route_topk, route_score, route_renorm, route_n_shared;
+  float route_shared_w;
+  int route_cap;             // T * (topk + n_shared) + (route_E + n_shared) * 15
+  int route_keep_off;        // LDS offset of the kept tables (set by the launcher)
+  int32_t* out_ids;
+  float* out_weights;
+  int32_t *out_counts, *out_offsets, *out_sorted, *out_block_expert, *out_num_padded;
 };
 
 __device__ __forceinline__ size_t wsc_index(const GemmParams& p, int e, int row) {
@@ -92,6 +103,10 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, in
 // Router + align-sort in a single one-workgroup launch; only when route_sort_fusable(T, E, K)
 // (E routed experts, K = topk + n_shared), else hipErrorInvalidValue.
 bool route_sort_fusable(int T, int E, int K);
+// Whether stage 1 can run with the router + sort fused in (16-row blocks, the persistent
+// kernel, LDS for the tile, the route scratch and the kept tables); K_dim = H, T tokens,
+// E routed experts, topk, n_shared.
+bool route_stage1_fusable(int afmt, int K_dim, int T, int E, int topk, int n_shared);
 hipError_t launch_route_sort(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
                              float shared_w, int bm, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
                              int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);

@@ -22,9 +22,10 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 constexpr int kSmallE = 64;  // route_tile_small serves E <= kSmallE
 
 // Weight of routed slot j of a token: sv = the token's k winning logits in rank order,
-// row = all E logits of the token (the full softmax sum runs over them in id order).
-__device__ __forceinline__ float slot_weight(const float* sv, int j, int topk, int score, int renorm,
-                                             const float* row, int E) {
+// row(i) = logit i of the token (the full softmax sum runs over them in id order).
+template <class Row>
+__device__ __forceinline__ float slot_weight(const float* sv, int j, int topk, int score, int renorm, Row row,
+                                             int E) {
   const float top_v = sv[0];
   auto f = [&](float x) { return score == 0 ? expf(x - top_v) : 1.0f / (1.0f + expf(-x)); };
   const float s = f(sv[j]);
@@ -36,7 +37,7 @@ __device__ __forceinline__ float slot_weight(const float* sv, int j, int topk, i
   } else if (score == 0) {
     denom = 0.0f;
 #pragma unroll 8
-    for (int i = 0; i < E; ++i) denom += expf(row[i] - top_v);
+    for (int i = 0; i < E; ++i) denom += expf(row(i) - top_v);
   }
   return (score == 0 || renorm) ? s / denom : s;
 }
@@ -71,7 +72,8 @@ __device__ __forceinline__ void route_tile_small(const float* lg, int t0, int nt
     float wt;
     if (j < topk) {
       id = sel_id[t * KP + j];
-      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, lg + t * E, E);
+      const float* lrow = lg + t * E;
+      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, [&](int i) { return lrow[i]; }, E);
     } else {
       id = E + (j - topk);
       wt = shared_w;

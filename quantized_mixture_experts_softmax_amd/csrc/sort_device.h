@@ -74,60 +74,112 @@ struct RouteSortOut {
   int32_t* num_padded;
 };
 
-// LDS bytes route_sort_block needs: logits [T][E + 1], the winners [T * topk] (value and
-// expert), selection masks and group prefixes [E][ceil(T / 64)], counts and offsets of
-// the E + n_shared experts, and the scan's wave sums.
+// Rank key of expert e's logit v: larger keys rank first.  The high word is the logit's
+// bits mapped to an unsigned order (-0 folded into +0, so equal logits have equal high
+// words), the low word ~e, so of two equal logits the lower id ranks first: one 64-bit
+// compare decides "ranks before" by value, then id.  Every key of a finite logit is > 0.
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~e;
+}
+// The logit a key was made from (+0 for -0: the weights computed from it are the same).
+__device__ __forceinline__ float rank_key_value(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+// LDS bytes route_sort_block needs: rank keys [T][E + 1], the winners [T * topk] (value
+// and expert), selection masks and group prefixes [E][ceil(T / 64)], counts and offsets
+// of the E + n_shared experts, the scan's wave sums, and 128 bytes of slack (the rank
+// pass reads whole batches of 16 keys; reads past a row's end in the last batch are not
+// used).
 __host__ __device__ constexpr size_t route_sort_lds_bytes(int T, int E, int topk, int n_shared, int groups) {
-  return ((size_t)T * (E + 1) * 4 + (size_t)T * topk * 8 + 8 + (size_t)E * groups * 12 +
-          (size_t)(2 * (E + n_shared) + 1) * 4 + (size_t)kSortWaves * 4 + 4 + 15) / 16 * 16;
+  return ((size_t)T * (E + 1) * 8 + (size_t)T * topk * 8 + 8 + (size_t)E * groups * 12 +
+          (size_t)(2 * (E + n_shared) + 1) * 4 + (size_t)kSortWaves * 4 + 4 + 128 + 15) / 16 * 16;
 }
 // Largest batch route_sort_block serves: T * E <= kFuseLogits, T * (topk + shared) <=
 // kSortChunk, E <= kSmallE, shared <= 32, so T * (E + 1) <= kFuseLogits + kSortChunk and
 // E * groups <= kFuseLogits / 64 + kSmallE.
 constexpr size_t kRouteSortLdsMax =
-    ((size_t)(kFuseLogits + kSortChunk) * 4 + (size_t)kSortChunk * 8 + 8 + (size_t)(kFuseLogits / 64 + kSmallE) * 12 +
-     (size_t)(2 * (kSmallE + 32) + 1) * 4 + (size_t)kSortWaves * 4 + 4 + 15) / 16 * 16;
+    ((size_t)(kFuseLogits + kSortChunk) * 8 + (size_t)kSortChunk * 8 + 8 + (size_t)(kFuseLogits / 64 + kSmallE) * 12 +
+     (size_t)(2 * (kSmallE + 32) + 1) * 4 + (size_t)kSortWaves * 4 + 4 + 128 + 15) / 16 * 16;
 
 // Router + align-sort of a small batch (E <= kSmallE, T * K <= kSortChunk, T * E <=
-// kFuseLogits) by one kSortThreads workgroup, all intermediates in the LDS at `lds`.
-// Lane t of a wave task counts the experts ranking before e in its token (an expert
-// j < e ranks before on >=, j > e on >: the id tie rule); an expert is chosen at most
-// once per token, so the masks' popcount prefix is the slot's stable row.
+// kFuseLogits) by one kSortThreads workgroup, all intermediates in the LDS at `lds`
 // (route_sort_lds_bytes(T, E, topk, n_shared, ceil(T / 64)) bytes, 16-byte aligned).
-// Expert-major: wave task
-// (expert e, group of 64 tokens) ranks each token's logit of e against the token's row
-// staged in LDS; the ballot of the winning lanes is the expert's selection mask for the
-// group, so the stable row of slot (t, j) inside its expert is a popcount prefix of the
-// masks.  Shared experts are chosen by every token, at position t.  The ids, weights and
-// sort equal those of the separate router and align-sort kernels.
+// Expert-major: wave task (expert e, group of 64 tokens) counts, for each token (lane),
+// the experts whose rank key exceeds e's (rank_key: a larger logit, or an equal one with a
+// lower id); the ballot of the lanes with a count below topk is the expert's selection
+// mask for the group.  An expert is chosen at most once per token, so the stable row of
+// slot (t, j) inside its expert is a popcount prefix of the masks.  Shared experts are
+// chosen by every token, at position t.  The ids, weights and sort equal those of the
+// separate router and align-sort kernels.
 __device__ __forceinline__ void route_sort_block(const float* __restrict__ logits, int T, int E, int topk, int score,
                                                  int renorm, int n_shared, float shared_w, int bm, int cap,
                                                  uint8_t* lds, const RouteSortOut& o) {
-  const int tid = (int)threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int KP = topk + n_shared, Et = E + n_shared, n = T * KP, G = (T + kWave - 1) / kWave, ld = E + 1;
-  float* lg = (float*)lds;                                   // [T][E + 1]
-  float* sel_v = lg + (size_t)T * ld;                        // [T][topk]
+  const int tid = (int)threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: task bounds and addresses stay scalar
+  const int KP = topk + n_shared, Et = E + n_shared, n = T * KP, G = (T + kWave - 1) / kWave;
+  // (offsets from `lds`, which is 16-byte aligned: an integer round trip of the pointer
+  // would lose its LDS address space and turn every access into a flat one)
+  const int ld = E + 1;                                      // key row stride (spreads the lanes over banks)
+  uint64_t* key = (uint64_t*)lds;                            // [T][E + 1]
+  float* sel_v = (float*)(key + (size_t)T * ld + 16);        // [T][topk] (after 128 bytes of slack)
   int* sel_e = (int*)(sel_v + (size_t)T * topk);             // [T][topk]
-  unsigned long long* mask = (unsigned long long*)(((uintptr_t)(sel_e + (size_t)T * topk) + 7) & ~(uintptr_t)7);
+  const size_t mask_off = ((size_t)T * ld * 8 + 128 + (size_t)T * topk * 8 + 7) & ~(size_t)7;
+  unsigned long long* mask = (unsigned long long*)(lds + mask_off);  // [E][G]
   int* pre = (int*)(mask + (size_t)E * G);                   // [E][G]
   int* cnt = pre + (size_t)E * G;                            // [Et]
   int* offs = cnt + Et;                                      // [Et + 1]
   int* wsum = offs + Et + 1;                                 // [kSortWaves]
   int* grand_total = wsum + kSortWaves;
 
-  for (int i = tid; i < T * E; i += kSortThreads) {
-    const int t = i / E;
-    lg[t * ld + (i - t * E)] = logits[i];
+  {
+    // all of a thread's loads are issued before the first LDS store (T * E <= kFuseLogits)
+    constexpr int kPer = kFuseLogits / kSortThreads;
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kSortThreads;
+      v[k] = i < T * E ? logits[i] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kSortThreads;
+      if (i < T * E) {
+        const int t = i / E, e = i - t * E;
+        key[(size_t)t * ld + e] = rank_key(v[k], e);
+      }
+    }
   }
   __syncthreads();
   for (int task = w; task < E * G; task += kSortWaves) {  // wave-uniform
     const int e = task / G, g = task - e * G, t = g * kWave + lane;
     const bool ok = t < T;
-    const float* row = lg + (ok ? t : 0) * ld;
-    const float v = row[e];
+    const uint64_t* row = key + (size_t)(ok ? t : 0) * ld;
+    const uint64_t ke = row[e];
+    // experts ranking before e: keys above e's.  Whole batches of 16 keys read with
+    // immediate offsets from one base and counted without bound checks; only the last,
+    // partial batch checks its (wave-uniform) bound, its reads past the row unused.
     int rank = 0;
-    for (int j = 0; j < e; ++j) rank += row[j] >= v ? 1 : 0;
-    for (int j = e + 1; j < E; ++j) rank += row[j] > v ? 1 : 0;
+    const int full = E & ~15;
+    for (int j0 = 0; j0 < full; j0 += 16) {
+      uint64_t x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] = row[j0 + k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rank += x[k] > ke ? 1 : 0;
+    }
+    if (full < E) {
+      uint64_t x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] = row[full + k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rank += (full + k < E && x[k] > ke) ? 1 : 0;
+    }
+    const float v = rank_key_value(ke);
     const bool sel = ok && rank < topk;
     const unsigned long long m = __ballot(sel);
     if (lane == 0) mask[task] = m;
@@ -137,23 +189,48 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
     }
   }
   __syncthreads();
-  // per-expert counts (shared experts: every token) and group prefixes
-  if (tid < Et) {
-    int c = T;
-    if (tid < E) {
-      c = 0;
-      for (int g = 0; g < G; ++g) {
-        pre[tid * G + g] = c;
-        c += __popcll(mask[tid * G + g]);
+  // Per-expert counts (shared experts: every token), group prefixes and padded offsets,
+  // by wave 0 alone: Et <= kSmallE + 32 <= 2 * kWave experts, expert lane + 64 h in
+  // element h of a lane, scanned lane by lane (h = 0 first), one barrier in all.
+  if (w == 0) {
+    int c[2], pd[2], s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = lane + kWave * h;
+      int cc = e < Et ? T : 0;
+      if (e < E) {
+        cc = 0;
+        for (int g = 0; g < G; ++g) {
+          pre[e * G + g] = cc;
+          cc += __popcll(mask[e * G + g]);
+        }
+      }
+      c[h] = cc;
+      pd[h] = (cc + bm - 1) / bm * bm;
+      s[h] = pd[h];
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int n0 = __shfl_up(s[0], o, kWave), n1 = __shfl_up(s[1], o, kWave);
+      if (lane >= o) {
+        s[0] += n0;
+        s[1] += n1;
       }
     }
-    cnt[tid] = c;
+    const int tot0 = __shfl(s[0], kWave - 1, kWave);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = lane + kWave * h;
+      if (e < Et) {
+        cnt[e] = c[h];
+        offs[e] = (h ? tot0 : 0) + s[h] - pd[h];
+      }
+    }
+    if (lane == kWave - 1) {
+      offs[Et] = tot0 + s[1];
+      *grand_total = tot0 + s[1];
+    }
   }
-  __syncthreads();
-  const int padded = tid < Et ? (cnt[tid] + bm - 1) / bm * bm : 0;
-  const int off = block_exclusive_scan(padded, wsum, grand_total);
-  if (tid < Et) offs[tid] = off;
-  if (tid == 0) offs[Et] = *grand_total;
   __syncthreads();
   const int total = *grand_total;
   if (tid < Et) {
@@ -171,7 +248,8 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
     float wt;
     if (j < topk) {
       e = sel_e[t * topk + j];
-      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, lg + t * ld, E);
+      const uint64_t* krow = key + (size_t)t * ld;
+      wt = slot_weight(sel_v + t * topk, j, topk, score, renorm, [&](int i) { return rank_key_value(krow[i]); }, E);
       const int g = t / kWave, l = t % kWave;
       const unsigned long long below = l ? (~0ull >> (kWave - l)) : 0ull;
       pos = offs[e] + pre[e * G + g] + __popcll(mask[e * G + g] & below);

@@ -163,3 +163,25 @@ def test_tiled_weight_bytes_and_validation(lib):
     assert lib.moe_tile_weights(7, 2, 32, 64, P(FAKE), P(FAKE), P(FAKE), None) == B.MOE_EINVAL
     fwd = lambda a: lib.moe_experts_forward(ctypes.byref(a), None)
     assert fwd(_args(weight_layout=5)) == B.MOE_EINVAL
+
+
+def test_layer_forward_rejects(lib):
+    """moe_layer_forward validates the forward arguments and the routing arguments on
+    the host; every call below breaks one rule and launches nothing."""
+    P = ctypes.c_void_p
+    f = lambda a, *r: lib.moe_layer_forward(ctypes.byref(a), *r)
+    ok_route = [P(FAKE), 0, 1, 0, 1.0, P(FAKE), P(FAKE), None]
+    def route_with(i, v):
+        r = list(ok_route)
+        r[i] = v
+        return r
+    assert f(_args(H=100), *ok_route) == B.MOE_EINVAL                      # forward shape rule
+    assert f(_args(), *route_with(3, 2)) == B.MOE_EINVAL                    # n_shared == K
+    assert "n_shared" in B.moe_last_error()
+    assert f(_args(), *route_with(3, -1)) == B.MOE_EINVAL
+    assert f(_args(), *route_with(0, None)) == B.MOE_EINVAL                 # NULL logits with T > 0
+    assert "moe_layer_forward" in B.moe_last_error()
+    assert f(_args(), *route_with(1, 7)) == B.MOE_EINVAL                    # unknown score
+    assert f(_args(), *route_with(5, None)) == B.MOE_EINVAL                 # expert_counts NULL
+    assert f(_args(), *route_with(0, P(FAKE + 2))) == B.MOE_EINVAL          # misaligned logits
+    assert f(_args(K=3, E_total=2), *ok_route) == B.MOE_EINVAL              # topk > routed experts

@@ -88,6 +88,30 @@ def test_route_align(case):
     assert int(srt["num_padded"].cpu()[0]) == ref["num_padded"]
 
 
+@pytest.mark.parametrize("T,E,k,score,ns", [(64, 32, 4, "softmax", 0), (200, 40, 6, "sigmoid", 1),
+                                            (128, 64, 32, "softmax", 0), (37, 8, 3, "softmax", 2)])
+def test_route_align_ties(T, E, k, score, ns):
+    """Logits on a coarse grid (many equal values per token, signed zeros included): the
+    ids follow the value-then-lower-id rule, on the fused and the separate paths."""
+    say(f"route_align ties T={T} E={E} k={k} {score} shared={ns}")
+    logits = make_logits(T, E, "ties", 900 + T + E)
+    logits[::3, : E // 2] = -0.0
+    logits[1::3, E // 2:] = 0.0
+    sw = 0.5 if ns else 1.0
+    lg = to_dev(logits)
+    ids, w, srt = B.moe_route_align(lg, k, 16, score, True, ns, sw)
+    ids2, w2 = B.moe_route_topk(lg, k, score, True, ns, sw)
+    srt2 = B.moe_align_sort(ids2, E + ns, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    for key in ("expert_counts", "expert_offsets", "sorted_slots", "block_expert", "num_padded"):
+        assert torch.equal(srt[key], srt2[key]), key
+    sc = orc.SCORE_SOFTMAX if score == "softmax" else orc.SCORE_SIGMOID
+    ref_ids, ref_w = orc.route_topk(logits, k, sc, True, ns, sw)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-30)
+
+
 SORT_CASES = [(64, 2, 8, 16), (64, 4, 32, 16), (64, 4, 32, 32), (8192, 4, 128, 128), (8192, 4, 128, 64),
               (4096, 9, 257, 128), (1, 2, 8, 16), (16, 2, 8, 16), (256, 2, 8, 64), (4096, 2, 8, 128),
               (1000, 5, 1024, 16), (0, 4, 32, 16), (20000, 3, 7, 32)]
