@@ -167,6 +167,9 @@ def main() -> int:
     ap.add_argument("--ep-share", type=int, default=1,
                     help="G > 1: time device 0's share of an expert-parallel layer over G devices (experts "
                          "[0, E/G) plus the replicated shared experts; all T tokens routed globally)")
+    ap.add_argument("--route", choices=["fused", "separate"], default="fused",
+                    help="fused: moe_layer_forward (small batches routed inside stage 1); separate: "
+                         "moe_route_align, then moe_experts_forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=10,
@@ -238,6 +241,7 @@ def main() -> int:
                                  I=w.I, E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
                                  score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                                  n_shared=w.n_shared, shared_weight=w.shared_weight, block_m=args.block_m,
+                                 fuse_route=args.route == "fused",
                                  tiled=args.layout == "tiled", grouped=grouped, act=act, expert_map=emap))
     x = torch.from_numpy(data["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     logits = t(data["logits"])
@@ -315,6 +319,7 @@ def main() -> int:
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
                    "weight_layout": args.layout,
                    "router_kind": "grouped (8 groups, 4 kept, bias, scaling 2.5)" if grouped else "plain top-k",
+                   "route_path": args.route,
                    "activation": "swiglu-oai, interleaved w13, biases" if act else "silu-and-mul",
                    "ep_share": (f"device 0 of EP{args.ep_share}: {w.E // args.ep_share} routed + {w.n_shared} "
                                 f"shared experts; value = T / this device's step time") if emap is not None else None},
