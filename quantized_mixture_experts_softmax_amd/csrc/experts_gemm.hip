@@ -1331,8 +1331,11 @@ constexpr size_t kPersistLdsFusedMax = 160 * 1024;
 #ifndef MOE_PERSIST_DEPTH_F4
 #define MOE_PERSIST_DEPTH_F4 6
 #endif
+#ifndef MOE_PERSIST_DEPTH_F4A4  // MXFP4 weights with MXFP4 activations: the A operand needs more registers
+#define MOE_PERSIST_DEPTH_F4A4 4
+#endif
 #ifndef MOE_PERSIST_DEPTH_F8
-#define MOE_PERSIST_DEPTH_F8 3
+#define MOE_PERSIST_DEPTH_F8 2
 #endif
 #ifndef MOE_PERSIST_DEPTH_F8B
 #define MOE_PERSIST_DEPTH_F8B 2
@@ -1395,7 +1398,8 @@ bool route_stage1_fusable(int afmt, int K_dim, int T, int E, int topk, int n_sha
 template <int STAGE, int WF, int AF, int WL, int EPI, int RS>
 static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t stream) {
   constexpr int WAVES = MOE_PERSIST_WAVES;
-  constexpr int D = (WF == kWMxfp4) ? MOE_PERSIST_DEPTH_F4 : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
+  constexpr int D = (WF == kWMxfp4) ? (AF == kAMxfp4 ? MOE_PERSIST_DEPTH_F4A4 : MOE_PERSIST_DEPTH_F4)
+                                    : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
   if (p.num_blocks == 0) return hipSuccess;
   auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI, RS>;
   static bool attr_set = false;
