@@ -863,16 +863,6 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
   return ((n > 63 ? 63 : n) & 0xF) | (((n > 63 ? 63 : n) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations,
-// not for its global loads in flight (__syncthreads waits for those too, which would
-// drain the weight prefetch ring).  The empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Direct global -> LDS load of 16 bytes per lane: the wave's 64 x 16 bytes land
 // contiguously at dst (wave-uniform).  Counted by vmcnt like any other load.
@@ -941,7 +931,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
                          first ? p.out_counts : nullptr, first ? p.out_offsets : nullptr, rs_sorted, rs_owner, rs_total};
     route_sort_block(p.logits, p.T, p.route_E, p.route_topk, p.route_score, p.route_renorm, p.route_n_shared,
                      p.route_shared_w, BM, p.route_cap, smem, o);
-    __syncthreads();
+    lds_barrier();
     npad = *rs_total;
     if (first) {
       for (int i = (int)threadIdx.x; i < p.route_cap; i += kThreads) p.out_sorted[i] = rs_sorted[i];

@@ -92,4 +92,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not
+// for its global loads in flight (__syncthreads waits for those too, which would drain
+// a weight prefetch ring).  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace moe

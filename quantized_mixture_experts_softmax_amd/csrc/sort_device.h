@@ -116,7 +116,23 @@ constexpr size_t kRouteSortLdsMax =
 // slot (t, j) inside its expert is a popcount prefix of the masks.  Shared experts are
 // chosen by every token, at position t.  The ids, weights and sort equal those of the
 // separate router and align-sort kernels.
-__device__ __forceinline__ void route_sort_block(const float* __restrict__ logits, int T, int E, int topk, int score,
+// The logits a thread of route_sort_block stages: element tid + k * kSortThreads of the
+// [T, E] array.
+struct RouteLogits {
+  float v[kFuseLogits / kSortThreads];
+};
+__device__ __forceinline__ void route_sort_load(const float* __restrict__ logits, int T, int E, RouteLogits& r) {
+  const int tid = (int)threadIdx.x, n = T * E;
+  if (n == 0) return;  // (uniform) logits may be NULL
+  // clamped, unconditional loads: straight-line code keeps them all in flight together
+  // (elements past n are loaded again and not used)
+#pragma unroll
+  for (int k = 0; k < kFuseLogits / kSortThreads; ++k) r.v[k] = logits[min(tid + k * kSortThreads, n - 1)];
+}
+
+// Its barriers order LDS only (all exchange between threads goes through LDS), so global
+// loads in flight are not waited for there.
+__device__ __forceinline__ void route_sort_block(const RouteLogits& lv, int T, int E, int topk, int score,
                                                  int renorm, int n_shared, float shared_w, int bm, int cap,
                                                  uint8_t* lds, const RouteSortOut& o) {
   const int tid = (int)threadIdx.x, lane = lane_id();
@@ -136,25 +152,15 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
   int* wsum = offs + Et + 1;                                 // [kSortWaves]
   int* grand_total = wsum + kSortWaves;
 
-  {
-    // all of a thread's loads are issued before the first LDS store (T * E <= kFuseLogits)
-    constexpr int kPer = kFuseLogits / kSortThreads;
-    float v[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kSortThreads;
-      v[k] = i < T * E ? logits[i] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kSortThreads;
-      if (i < T * E) {
-        const int t = i / E, e = i - t * E;
-        key[(size_t)t * ld + e] = rank_key(v[k], e);
-      }
+  for (int k = 0; k < kFuseLogits / kSortThreads; ++k) {
+    const int i = tid + k * kSortThreads;
+    if (i < T * E) {
+      const int t = i / E, e = i - t * E;
+      key[(size_t)t * ld + e] = rank_key(lv.v[k], e);
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int task = w; task < E * G; task += kSortWaves) {  // wave-uniform
     const int e = task / G, g = task - e * G, t = g * kWave + lane;
     const bool ok = t < T;
@@ -188,7 +194,7 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
       sel_v[t * topk + rank] = v;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Per-expert counts (shared experts: every token), group prefixes and padded offsets,
   // by wave 0 alone: Et <= kSmallE + 32 <= 2 * kWave experts, expert lane + 64 h in
   // element h of a lane, scanned lane by lane (h = 0 first), one barrier in all.
@@ -231,7 +237,7 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
       *grand_total = tot0 + s[1];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int total = *grand_total;
   if (tid < Et) {
     if (o.counts) o.counts[tid] = cnt[tid];
@@ -265,4 +271,15 @@ __device__ __forceinline__ void route_sort_block(const float* __restrict__ logit
   if (o.sorted) fill_pads_owners(offs, cnt, Et, total, n, bm, cap, tid, kSortThreads, o.sorted, o.block_expert);
 }
 
+}  // namespace moe
+
+namespace moe {
+// Loads the logits, then routes and sorts (route_sort_load + route_sort_block).
+__device__ __forceinline__ void route_sort_block(const float* __restrict__ logits, int T, int E, int topk, int score,
+                                                 int renorm, int n_shared, float shared_w, int bm, int cap,
+                                                 uint8_t* lds, const RouteSortOut& o) {
+  RouteLogits lv;
+  route_sort_load(logits, T, E, lv);
+  route_sort_block(lv, T, E, topk, score, renorm, n_shared, shared_w, bm, cap, lds, o);
+}
 }  // namespace moe
