@@ -282,9 +282,10 @@ typedef struct moe_forward_args {
                                                     1: gate_n, up_n alternate (the INTERLEAVE gate
                                                     mode of [rocm_aiter_moe]
                                                     mxfp4_w4a16_extra_kwargs); not for FP8_BLOCK128 */
-  const uint16_t* w1_bias;                       /* bf16 [E_total, 2I] in w1 row order, or NULL */
-  const uint16_t* w2_bias;                       /* bf16 [E_total, H], or NULL ([mxfp4.py]
-                                                    create_weights: w13_bias, w2_bias) */
+  const uint16_t* w1_bias;                       /* bf16 [E_total, 2I] in w1 row order, or NULL;
+                                                    4-byte aligned (bias pairs are loaded as words) */
+  const uint16_t* w2_bias;                       /* bf16 [E_total, H], or NULL, 4-byte aligned
+                                                    ([mxfp4.py] create_weights: w13_bias, w2_bias) */
   int apply_router_weight_on_input;              /* 1: topk_weights scale both stage-1
                                                     projections and the sum over slots is
                                                     unweighted; needs K == 1 ([rocm_aiter_moe]

@@ -870,6 +870,11 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
   typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 16, 0, 0);
 }
+// The same with 4 bytes per lane: 256 contiguous bytes at dst.
+__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 4, 0, 0);
+}
 
 // ---------------------------------------------------------------------------------
 // Persistent 16-row kernel (the decode shape, activation tile in LDS).  The grid is
@@ -956,7 +961,12 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   uint8_t* lds_a = smem;
   int* lds_row = (int*)(smem + (size_t)16 * upr * 16);  // activation row of each tile row (-1: pad)
   int* lds_slot = lds_row + 16;                          // sorted slot of each tile row
+  float* lds_fw = (float*)(lds_slot + 16);               // router weight of each tile row (weight on input)
   uint8_t* lds_sc = (uint8_t*)(lds_slot + 32);
+  // biases of the phase's units, bf16, [unit - ua][tile][16 columns]: staged in the
+  // prologue so that no bias load is waited for in the stream (a load issued at a unit's
+  // end would wait for every ring load in flight)
+  uint16_t* lds_bias = (uint16_t*)(smem + p.bias_lds_off);
   float* lds_part = (float*)(smem + tile16_lds_bytes(AF, K));  // [WAVES][NT*4][64]
   const MOE_GLOBAL uint8_t* zp = (const MOE_GLOBAL uint8_t*)kZeroPage;
 
@@ -1020,6 +1030,10 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
       if (STAGE == 1) lds_row[tid] = slot_v < TK ? slot_v / p.slots_per_token : -1;
     }
     if (STAGE == 1) lds_barrier();
+    float fw_v = 0.0f;  // weight on input: the row's router weight (0 for pad rows), staged with the slot
+    if (EPI && STAGE == 1 && p.weight_on_input && tid < BM)
+      fw_v = ldf(p.topk_weights, (size_t)(slot_v < TK ? slot_v : 0), slot_v < TK);
+    // bias slice: direct global -> LDS loads of bias pairs, issued with the tile below
 
     // activation scales (quantised formats) go through registers, issued before the tile
     constexpr int kScPer = (AF == kAMxfp4) ? 8 : 1;  // per thread: 16 x 4 x nch bytes <= 8 x kThreads
@@ -1050,7 +1064,21 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
       }
     }
 
-    // ---- activation tile -> LDS (direct loads), then the ring ----
+    // ---- bias slice and activation tile -> LDS (direct loads), then the ring ----
+    if constexpr (EPI) {
+      // lane l of direct load i moves the bias pair of slice entries 2 (64 i + l), +1: unit
+      // u, tile t, columns c, c + 1 (c even, so the pair is 4-byte aligned and never
+      // crosses a 16-column tile); past the phase, or past N in stage 2, the zero page
+      const int ndw = p.bias ? (ub - ua) * 16 : 0;
+      for (int i = wv; i * 64 < ndw; i += WAVES) {
+        const int d = i * 64 + lane, q = 2 * d;
+        const int col = trow_of(q >> 5, (q >> 4) & 1) + (q & 15);
+        const bool ok = d < ndw && (STAGE == 1 || col < p.N);
+        const MOE_GLOBAL uint8_t* src =
+            ok ? (const MOE_GLOBAL uint8_t*)p.bias + ((size_t)e * p.Nw + col) * 2 : zp;
+        dma4((const void*)src, (uint8_t*)lds_bias + (size_t)i * 256);
+      }
+    }
     for (int i = wv; i < n_dma; i += WAVES) {
       const int v = i * 64 + lane;
       const int r = v / upr, pv = v - r * upr;
@@ -1069,7 +1097,11 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
     __builtin_amdgcn_sched_barrier(0);
     // at most the ring's loads outstanding: this wave's tile loads and scales have landed
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRingLoads));
-    if (tid < BM) lds_slot[tid] = slot_v;
+    if (tid < BM) {
+      lds_slot[tid] = slot_v;
+      if (EPI && STAGE == 1) lds_fw[tid] = fw_v;
+    }
+
     if constexpr (AF == kAFp8G128) {
       if (tid < BM * nch) ((float*)lds_sc)[tid] = sc_f;
     } else if constexpr (AF == kAMxfp4) {
@@ -1153,8 +1185,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               const int row = 4 * g + rr;
               float v = acc[t][rr];
               if constexpr (WF == kWFp8Channel) v = v * ((const float*)lds_sc)[row] * csc[t];
-              if (EPI && p.weight_on_input) v *= fc1_weight(p, lds_slot[row]);
-              if (EPI && p.bias) v += bias_of(p, e, trow_of(u, t) + li);
+              if (EPI && p.weight_on_input) v *= lds_fw[row];
+              if (EPI && p.bias) v += __uint_as_float((uint32_t)lds_bias[u * 32 + t * 16 + li] << 16);
               const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
               if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
             }
@@ -1171,13 +1203,13 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               uv = uv * as * csc[1];
             }
             if (EPI && p.weight_on_input) {
-              const float fw = fc1_weight(p, lds_slot[row]);
+              const float fw = lds_fw[row];
               gv *= fw;
               uv *= fw;
             }
             if (EPI && p.bias) {
-              gv += bias_of(p, e, trow_of(u, 0) + li);
-              uv += bias_of(p, e, trow_of(u, 1) + li);
+              gv += __uint_as_float((uint32_t)lds_bias[u * 32 + li] << 16);
+              uv += __uint_as_float((uint32_t)lds_bias[u * 32 + 16 + li] << 16);
             }
             p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
           }
@@ -1195,7 +1227,7 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
             if (col >= p.N) continue;
             float v = acc[t][rr];
             if constexpr (WF == kWFp8Channel) v = v * as * csc[t];
-            if (EPI && p.bias) v += bias_of(p, e, col);
+            if (EPI && p.bias) v += __uint_as_float((uint32_t)lds_bias[u * 32 + t * 16 + li] << 16);
             p.ybuf[(size_t)slot * p.N + col] = v;
           }
         }
@@ -1363,15 +1395,23 @@ static size_t persist_lds_limit() {
   return std::min((size_t)lim[dev], kPersistLdsFusedMax);
 }
 
+// Bytes of the persistent kernel's bias slice: one phase covers at most the U units of a
+// block, 32 bf16 biases each (stage 1: N = I columns in gate/up pairs; stage 2: N = H),
+// written by direct loads of 256 bytes.
+static size_t bias_slice_bytes(int stage, int N) {
+  const size_t units = stage == 1 ? (size_t)(N + 15) / 16 : (size_t)(N + 31) / 32;
+  return (units * 32 * 2 + 255) / 256 * 256;
+}
+
 // LDS of the persistent stage-1 kernel with the route + sort fused in: the route
-// scratch overlaps the tile and partial-sum region; the kept tables (sorted rows [cap],
-// block owners [cap / 16], padded total) follow both.  False when the batch is too
-// large for the one-workgroup route + sort or the LDS does not fit.
-static bool route_stage1_lds(int afmt, int K_dim, int T, int E, int topk, int n_shared, size_t* keep_off,
-                             size_t* total) {
+// scratch overlaps the tile, partial-sum and bias region; the kept tables (sorted rows
+// [cap], block owners [cap / 16], padded total) follow all of them.  False when the batch
+// is too large for the one-workgroup route + sort or the LDS does not fit.
+static bool route_stage1_lds(int afmt, int K_dim, int N, bool bias, int T, int E, int topk, int n_shared,
+                             size_t* keep_off, size_t* total) {
   if (64 * MOE_PERSIST_WAVES != kSortThreads || !route_sort_fusable(T, E, topk + n_shared)) return false;
   const long cap = (long)T * (topk + n_shared) + (long)(E + n_shared) * 15;
-  const size_t base = persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES);
+  const size_t base = persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES) + (bias ? bias_slice_bytes(1, N) : 0);
   const size_t scratch = route_sort_lds_bytes(T, E, topk, n_shared, (T + kWave - 1) / kWave);
   const size_t off = (std::max(base, scratch) + 15) / 16 * 16;
   const size_t all = off + (size_t)(cap + cap / 16 + 1) * 4;
@@ -1380,9 +1420,10 @@ static bool route_stage1_lds(int afmt, int K_dim, int T, int E, int topk, int n_
   return all <= persist_lds_limit();
 }
 
-bool route_stage1_fusable(int afmt, int K_dim, int T, int E, int topk, int n_shared) {
+bool route_stage1_fusable(int afmt, int K_dim, int N, int T, int E, int topk, int n_shared, bool bias) {
   size_t off = 0, all = 0;
-  return T > 0 && route_stage1_lds(afmt, K_dim, T, E, topk, n_shared, &off, &all);
+  return T > 0 && persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES) <= kPersistLdsMax &&
+         route_stage1_lds(afmt, K_dim, N, bias, T, E, topk, n_shared, &off, &all);
 }
 
 template <int STAGE, int WF, int AF, int WL, int EPI, int RS>
@@ -1413,19 +1454,24 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
 template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
+    const size_t tile_lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
+    const bool bias = EPI && p_in.bias;
+    GemmParams p = p_in;
+    p.bias_lds_off = (int)tile_lds;  // the bias slice follows the tile and partial sums
     if constexpr (STAGE == 1 && 64 * MOE_PERSIST_WAVES == kSortThreads) {
       if (p_in.route) {
-        GemmParams p = p_in;
         size_t keep_off = 0, lds = 0;
-        if (!route_stage1_lds(AF, p.K, p.T, p.route_E, p.route_topk, p.route_n_shared, &keep_off, &lds))
+        if (tile_lds > kPersistLdsMax ||
+            !route_stage1_lds(AF, p.K, p.N, bias, p.T, p.route_E, p.route_topk, p.route_n_shared, &keep_off, &lds))
           return hipErrorInvalidValue;
         p.route_keep_off = (int)keep_off;
         return launch_persist<STAGE, WF, AF, WL, EPI, 1>(p, lds, stream);
       }
     }
-    const size_t lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
-    if (lds <= std::min(kPersistLdsMax, persist_lds_limit()))
-      return launch_persist<STAGE, WF, AF, WL, EPI, 0>(p_in, lds, stream);
+    // 16-row blocks whose activation tile fits run here (larger tiles: the K-split kernel)
+    const size_t lds = tile_lds + (bias ? bias_slice_bytes(STAGE, p_in.N) : 0);
+    if (tile_lds <= kPersistLdsMax && lds <= persist_lds_limit())
+      return launch_persist<STAGE, WF, AF, WL, EPI, 0>(p, lds, stream);
   }
   if (p_in.route) return hipErrorInvalidValue;  // the fused route + sort runs in the persistent kernel only
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging

@@ -342,9 +342,9 @@ moe_status experts_forward(const moe_forward_args* a, const FusedRoute* r, hipSt
   if (!aligned(a->hidden_states, 16) || !aligned(a->w1, 16) || !aligned(a->w2, 16) || !aligned(a->out, 16) ||
       !aligned(a->topk_weights, 4) || !aligned(a->w1_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) ||
       !aligned(a->w2_scale, a->wfmt == MOE_W_MXFP4 ? 1 : 4) || (a->a1_codes && !aligned(a->a1_codes, 16)) ||
-      (a->a1_scales && !aligned(a->a1_scales, 4)) || !aligned(a->w1_bias, 2) || !aligned(a->w2_bias, 2))
+      (a->a1_scales && !aligned(a->a1_scales, 4)) || !aligned(a->w1_bias, 4) || !aligned(a->w2_bias, 4))
     return fail(MOE_EINVAL, "moe_experts_forward: misaligned pointer (16 B for tensors, 4 B for fp32 arrays, "
-                            "2 B for biases)");
+                            "4 B for biases)");
   if (a->afmt != MOE_A_BF16 && (a->a1_codes == nullptr) != (a->a1_scales == nullptr))
     return fail(MOE_EINVAL, "moe_experts_forward: a1_codes and a1_scales go together");
   if (!a->workspace || a->workspace_bytes < L.total)
@@ -486,7 +486,7 @@ moe_status moe_layer_forward(const moe_forward_args* a, const float* router_logi
   // stage 1 on the persistent 16-row kernel routes and sorts the batch itself; the
   // router weight on the input is read by stage 1 and so needs the weights first
   if (a->block_m == 16 && !a->apply_router_weight_on_input &&
-      moe::route_stage1_fusable((int)a->afmt, a->H, a->T, E, topk, n_shared)) {
+      moe::route_stage1_fusable((int)a->afmt, a->H, a->I, a->T, E, topk, n_shared, a->w1_bias != nullptr)) {
     const FusedRoute r{router_logits, E, topk, (int)score, renormalize ? 1 : 0, n_shared, shared_weight,
                        expert_counts, expert_offsets};
     return experts_forward(a, &r, stream);

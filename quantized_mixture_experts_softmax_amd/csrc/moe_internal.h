@@ -56,6 +56,7 @@ struct GemmParams {
   float route_shared_w;
   int route_cap;             // T * (topk + n_shared) + (route_E + n_shared) * 15
   int route_keep_off;        // LDS offset of the kept tables (set by the launcher)
+  int bias_lds_off;          // persistent kernel with biases: LDS offset of a phase's bias slice (launcher)
   int32_t* out_ids;
   float* out_weights;
   int32_t *out_counts, *out_offsets, *out_sorted, *out_block_expert, *out_num_padded;
@@ -104,9 +105,9 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int K, int E, int bm, in
 // (E routed experts, K = topk + n_shared), else hipErrorInvalidValue.
 bool route_sort_fusable(int T, int E, int K);
 // Whether stage 1 can run with the router + sort fused in (16-row blocks, the persistent
-// kernel, LDS for the tile, the route scratch and the kept tables); K_dim = H, T tokens,
-// E routed experts, topk, n_shared.
-bool route_stage1_fusable(int afmt, int K_dim, int T, int E, int topk, int n_shared);
+// kernel, LDS for the tile, the bias slice, the route scratch and the kept tables); K_dim
+// = H, N = I, T tokens, E routed experts, topk, n_shared, bias: w1 biases present.
+bool route_stage1_fusable(int afmt, int K_dim, int N, int T, int E, int topk, int n_shared, bool bias);
 hipError_t launch_route_sort(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
                              float shared_w, int bm, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
                              int32_t* sorted, int32_t* block_expert, int32_t* num_padded, hipStream_t stream);

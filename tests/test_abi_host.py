@@ -129,6 +129,8 @@ def test_forward_rejects(lib):
     assert "workspace" in B.moe_last_error()
     assert fwd(_args(w1=None, workspace_bytes=1 << 40)) == B.MOE_EINVAL
     assert fwd(_args(hidden_states=FAKE + 8, workspace_bytes=1 << 40)) == B.MOE_EINVAL
+    assert fwd(_args(w1_bias=FAKE + 2, workspace_bytes=1 << 40)) == B.MOE_EINVAL  # biases: 4-byte aligned
+    assert "biases" in B.moe_last_error()
     assert lib.moe_supports(B.W_MXFP4, B.A_MXFP4_G32, 0, 2880, 2880) == B.MOE_OK
     assert lib.moe_supports(B.W_FP8_CHANNEL, B.A_FP8_G128, 0, 4096, 14336) == B.MOE_EUNSUPPORTED
 
