@@ -527,9 +527,14 @@ static int tensor_rows(const uint16_t* const* rows, size_t n_rows, int n, double
  * FP8 block ([rocm_aiter_moe] AiterFp8BlockExperts: 128x128 weight blocks):
  * value = e4m3(code) * scale[e][n/128][k/128].
  * FP8 channel ([rocm_aiter_moe] AiterFp8ChannelExperts: per output channel):
- * value = e4m3(code) * scale[e][n]. */
+ * value = e4m3(code) * scale[e][n].
+ * bf16 (the unquantised leaf, [rocm_aiter_moe] AiterExperts with no quantisation):
+ * value = the bf16 number itself, exact in fp64. */
 static void weight_row(int wfmt, const uint8_t* w, const void* scale, int e, int n, int N, int K, double* out) {
-  if (wfmt == ORC_W_MXFP4) {
+  if (wfmt == ORC_W_BF16) {
+    const uint16_t* row = (const uint16_t*)w + ((size_t)e * N + n) * (size_t)K;
+    for (int k = 0; k < K; ++k) out[k] = (double)orc_bf16_to_f32(row[k]);
+  } else if (wfmt == ORC_W_MXFP4) {
     const uint8_t* row = w + ((size_t)e * N + n) * (size_t)(K / 2);
     const uint8_t* srow = (const uint8_t*)scale + ((size_t)e * N + n) * (size_t)(K / 32);
     for (int k = 0; k < K; ++k) {
@@ -582,7 +587,7 @@ static double bias_at(const uint16_t* b, size_t i) { return b ? (double)orc_bf16
 static int layer_ok(const orc_layer* L) {
   if (!L || L->H <= 0 || L->I <= 0 || L->E_total <= 0 || L->K <= 0) return 0;
   if (L->H % 32 || L->I % 32) return 0;
-  if (L->wfmt < ORC_W_MXFP4 || L->wfmt > ORC_W_FP8_TENSOR) return 0;
+  if (L->wfmt < ORC_W_MXFP4 || L->wfmt > ORC_W_BF16) return 0;
   if (L->afmt < ORC_A_BF16 || L->afmt > ORC_A_FP8_TENSOR) return 0;
   if (L->act != ORC_ACT_SILU && L->act != ORC_ACT_SWIGLU_OAI) return 0;
   return 1;

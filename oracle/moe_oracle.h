@@ -12,6 +12,7 @@
  *   byte k/2 (low nibble = even k); scales s[E][N][K/32] are E8M0 bytes.
  *   FP8 weights: w[E][N][K] e4m3fn bytes; block scales [E][ceil(N/128)][ceil(K/128)]
  *   fp32, channel scales [E][N] fp32.
+ *   bf16 weights (unquantised): w[E][N][K] bf16 bit patterns (2 bytes each), no scales.
  *   w1 holds the fused gate/up projection: rows [0, I) are gate, [I, 2I) are up.
  *
  * Return value of every int function: 0 on success, -1 on bad arguments.
@@ -25,7 +26,7 @@ extern "C" {
 #endif
 
 /* weight formats */
-enum { ORC_W_MXFP4 = 0, ORC_W_FP8_BLOCK128 = 1, ORC_W_FP8_CHANNEL = 2, ORC_W_FP8_TENSOR = 3 };
+enum { ORC_W_MXFP4 = 0, ORC_W_FP8_BLOCK128 = 1, ORC_W_FP8_CHANNEL = 2, ORC_W_FP8_TENSOR = 3, ORC_W_BF16 = 4 };
 /* activation (GEMM input) formats */
 enum { ORC_A_BF16 = 0, ORC_A_MXFP4_G32 = 1, ORC_A_FP8_G128 = 2, ORC_A_FP8_TOKEN = 3, ORC_A_FP8_TENSOR = 4 };
 /* router score functions */

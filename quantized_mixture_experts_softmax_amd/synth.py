@@ -32,7 +32,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR = 0, 1, 2, 3
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR, W_BF16 = 0, 1, 2, 3, 4
 A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 
@@ -82,6 +82,7 @@ WORKLOADS = {
     "fp8-channel": Workload("fp8-channel", 4096, 4096, 14336, 8, 2, W_FP8_CHANNEL, A_FP8_TOKEN, seed=1004,
                             T_sweep=(1, 16, 256, 4096)),
     # per-tensor FP8 leaf at the fp8-channel shapes (not a configuration of its own)
+    "bf16-decode": Workload("bf16-decode", 64, 2880, 2880, 32, 4, W_BF16, A_BF16, logit_std=1.5, seed=1006),
     "fp8-tensor": Workload("fp8-tensor", 4096, 4096, 14336, 8, 2, W_FP8_TENSOR, A_FP8_TENSOR, seed=1005,
                            T_sweep=(1, 16, 256, 4096)),
 }
@@ -168,6 +169,18 @@ def _weight(w: Workload, N: int, K: int, seq_codes, rng_scales):
     from concurrent.futures import ThreadPoolExecutor
 
     E = w.E_total
+    if w.wfmt == W_BF16:
+        # unquantised: N(0, 1/K) per expert, rounded to bf16 (the bit patterns, uint16)
+        out = np.empty((E, N, K), np.uint16)
+        seqs_b = seq_codes.spawn(E)
+
+        def fill_b(e):
+            v = np.random.default_rng(seqs_b[e]).standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K))
+            out[e] = f32_to_bf16_bits(v)
+
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill_b, range(E)))
+        return out, None
     fp8 = w.wfmt != W_MXFP4
     kb = K if fp8 else K // 2
     codes = np.empty((E, N, kb), np.uint8)

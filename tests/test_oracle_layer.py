@@ -16,6 +16,8 @@ E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.f
 def decode_weights(wfmt, w, s, N, K):
     """[E, N, K] fp64 from the literal e2m1 table / torch's e4m3 decode."""
     E = w.shape[0]
+    if wfmt == synth.W_BF16:  # the bf16 number: its 16 bits are the top half of an fp32
+        return (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if wfmt == synth.W_MXFP4:
         nib = np.stack([w & 15, w >> 4], axis=-1).reshape(E, N, K)
         scale = np.ldexp(1.0, s.astype(np.int64) - 127)
@@ -94,7 +96,7 @@ def tiny(wfmt, afmt, T=4, H=64, I=32, E=4, k=2, n_shared=0, seed=7):
 
 FORMATS = [(synth.W_MXFP4, synth.A_BF16), (synth.W_MXFP4, synth.A_MXFP4_G32),
            (synth.W_FP8_BLOCK128, synth.A_FP8_G128), (synth.W_FP8_CHANNEL, synth.A_FP8_TOKEN),
-           (synth.W_FP8_BLOCK128, synth.A_BF16), (synth.W_FP8_CHANNEL, synth.A_BF16)]
+           (synth.W_FP8_BLOCK128, synth.A_BF16), (synth.W_FP8_CHANNEL, synth.A_BF16), (synth.W_BF16, synth.A_BF16)]
 
 
 @pytest.mark.parametrize("wfmt,afmt", FORMATS)
@@ -109,7 +111,7 @@ def test_forward_brute_force_fp64(orc, wfmt, afmt):
     assert np.max(np.abs(got - ref)) <= 1e-3 * rms
 
 
-@pytest.mark.parametrize("wfmt", [synth.W_MXFP4, synth.W_FP8_BLOCK128, synth.W_FP8_CHANNEL])
+@pytest.mark.parametrize("wfmt", [synth.W_MXFP4, synth.W_FP8_BLOCK128, synth.W_FP8_CHANNEL, synth.W_BF16])
 def test_top1_weight1_is_dense_gated_mlp(orc, wfmt):
     """With one routed slot of weight 1 the layer is W2 . (silu(Wg x) * (Wu x))."""
     wl = tiny(wfmt, synth.A_BF16, T=6, H=256, I=128, E=3, k=1)
@@ -131,7 +133,7 @@ def test_top1_weight1_is_dense_gated_mlp(orc, wfmt):
     sw = dict(data)
     sw["w1"] = np.ascontiguousarray(np.concatenate([data["w1"][:, wl.I:], data["w1"][:, :wl.I]], axis=1))
     sw["w1_scale"] = np.ascontiguousarray(np.concatenate([data["w1_scale"][:, wl.I:], data["w1_scale"][:, :wl.I]], axis=1)) \
-        if wfmt != synth.W_FP8_BLOCK128 else data["w1_scale"]
+        if wfmt not in (synth.W_FP8_BLOCK128, synth.W_BF16) else data["w1_scale"]
     other = orc.forward(layer_of(orc, wl, sw), data["x"], ids, w)
     assert not np.allclose(other, got)
 
@@ -255,3 +257,24 @@ def test_router_weight_on_input(orc, wfmt, afmt):
         assert np.max(np.abs(got[t] - ref)) <= 1e-3 * np.sqrt(np.mean(ref ** 2))
     weighted_out = orc.forward(plain, data["x"], ids, wt)
     assert not np.allclose(got, weighted_out, rtol=1e-3)
+
+
+def test_bf16_weights_scale_linearly(orc):
+    """Unquantised weights: doubling every w2 value (adding one to each bf16 exponent)
+    doubles the output exactly, and negating w1's up half negates it (silu(g) * (-u))."""
+    wl = tiny(synth.W_BF16, synth.A_BF16, T=5, H=64, I=32, E=3, k=2)
+    data = synth.make_all(wl)
+    ids, w = orc.route_topk(data["logits"], wl.topk)
+    L = layer_of(orc, wl, data)
+    base = orc.forward(L, data["x"], ids, w)
+    w2 = data["w2"].copy()
+    nz = (w2 & 0x7F80) != 0
+    w2[nz] = w2[nz] + np.uint16(0x80)  # exponent + 1 (no value here is near overflow)
+    dbl = orc.forward(orc.Layer(wl.H, wl.I, wl.E_total, wl.K, wl.wfmt, wl.afmt, data["w1"], None, w2, None),
+                      data["x"], ids, w)
+    assert np.array_equal(dbl, 2.0 * base)
+    w1 = data["w1"].copy()
+    w1[:, wl.I:] ^= np.uint16(0x8000)
+    neg = orc.forward(orc.Layer(wl.H, wl.I, wl.E_total, wl.K, wl.wfmt, wl.afmt, w1, None, data["w2"], None),
+                      data["x"], ids, w)
+    assert np.array_equal(neg, -base)
