@@ -73,6 +73,9 @@ def algorithmic(w, ids_np):
     if w.wfmt == synth.W_MXFP4:
         w1_per = 2 * w.I * (w.H // 2 + w.H // 32)
         w2_per = w.H * (w.I // 2 + w.I // 32)
+    elif w.wfmt == synth.W_BF16:
+        w1_per = 2 * w.I * w.H * 2
+        w2_per = w.H * w.I * 2
     elif w.wfmt == synth.W_FP8_BLOCK128:
         w1_per = 2 * w.I * w.H + 4 * ((2 * w.I + 127) // 128) * ((w.H + 127) // 128)
         w2_per = w.H * w.I + 4 * ((w.H + 127) // 128) * ((w.I + 127) // 128)
@@ -95,6 +98,8 @@ def mfma_dtype(w):
 
     if w.wfmt == synth.W_MXFP4:
         return "fp4" if w.afmt == synth.A_MXFP4_G32 else "bf16"
+    if w.wfmt == synth.W_BF16:
+        return "bf16"
     return "fp8"
 
 
@@ -157,7 +162,7 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=None, help="token count (fp8-channel sweep: 1, 16, 256, 4096)")
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--weight-copies", type=int, default=None)
-    ap.add_argument("--layout", choices=["tiled", "canonical"], default="tiled",
+    ap.add_argument("--layout", choices=["tiled", "canonical"], default=None,
                     help="weight layout: the kernel layout prepared once by moe_tile_weights, or canonical")
     ap.add_argument("--router", choices=["plain", "grouped"], default="plain",
                     help="grouped: group-limited router (8 groups, 4 kept, seeded correction bias, scaling 2.5)")
@@ -198,10 +203,20 @@ def main() -> int:
     if args.tokens:
         w = w.with_T(args.tokens)
     data = synth.make_all(w)
-    wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale"))
+    wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale") if data[k] is not None)
     # enough copies that one rotation is larger than twice the Infinity Cache
     copies = args.weight_copies or (1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1))
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    def t(a):  # host array -> device tensor (bf16 bit arrays as bf16; absent scales stay None)
+        if a is None:
+            return None
+        a = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
+        return (a.view(torch.bfloat16) if a.dtype == torch.int16 else a).to(dev)
+
+    if args.layout is None:
+        args.layout = "canonical" if w.wfmt == synth.W_BF16 else "tiled"
+    if w.wfmt == synth.W_BF16 and (args.layout == "tiled" or (args.block_m or 64) < 64):
+        print("bench.py: bf16 weights run on the canonical layout with 64- or 128-row blocks", file=sys.stderr)
+        return 2
     grouped = None
     if args.router == "grouped":
         if w.E % 8:
@@ -216,7 +231,8 @@ def main() -> int:
                   file=sys.stderr)
             return 2
         b1, b2 = synth.make_biases(w)
-        data = dict(data, w1=synth.interleave_rows(data["w1"], w.I), w1_scale=synth.interleave_rows(data["w1_scale"], w.I))
+        data = dict(data, w1=synth.interleave_rows(data["w1"], w.I),
+                    w1_scale=None if data["w1_scale"] is None else synth.interleave_rows(data["w1_scale"], w.I))
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
         act = dict(kind=B.ACT_SWIGLU_OAI, alpha=1.702, beta=1.0, limit=7.0, interleaved=True,
                    w1_bias=bf(synth.interleave_rows(b1, w.I)), w2_bias=bf(b2))
@@ -232,8 +248,9 @@ def main() -> int:
         m = np.full(w.E_total, -1, np.int32)
         m[mine] = np.arange(len(mine), dtype=np.int32)
         emap = torch.from_numpy(m).to(dev)
-        data = dict(data, **{k: np.ascontiguousarray(data[k][mine]) for k in ("w1", "w1_scale", "w2", "w2_scale")})
-        wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale"))
+        data = dict(data, **{k: np.ascontiguousarray(data[k][mine]) for k in ("w1", "w1_scale", "w2", "w2_scale")
+                             if data[k] is not None})
+        wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale") if data[k] is not None)
         copies = args.weight_copies or (1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1))
     layers = []
     for _ in range(copies):
@@ -312,8 +329,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic (seeded; random weight codes and scales, no checkpoint)",
-        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel', 'fp8-tensor'][w.wfmt]}-"
-                               f"{['w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token', 'a-fp8-tensor'][w.afmt]}",
+        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel', 'fp8-tensor', 'bf16'][w.wfmt]}-"
+                               f"{['a-bf16' if w.wfmt == synth.W_BF16 else 'w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token', 'a-fp8-tensor'][w.afmt]}",
                    "T": w.T, "H": w.H, "I": w.I, "experts": w.E, "shared_experts": w.n_shared, "topk": w.topk,
                    "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],

@@ -528,7 +528,7 @@ static int tensor_rows(const uint16_t* const* rows, size_t n_rows, int n, double
  * value = e4m3(code) * scale[e][n/128][k/128].
  * FP8 channel ([rocm_aiter_moe] AiterFp8ChannelExperts: per output channel):
  * value = e4m3(code) * scale[e][n].
- * bf16 (the unquantised leaf, [rocm_aiter_moe] AiterExperts with no quantisation):
+ * bf16 (the unquantised leaf, [rocm_aiter_moe] AiterUnquantizedExperts):
  * value = the bf16 number itself, exact in fp64. */
 static void weight_row(int wfmt, const uint8_t* w, const void* scale, int e, int n, int N, int K, double* out) {
   if (wfmt == ORC_W_BF16) {

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 SCORE = {"softmax": 0, "sigmoid": 1}
-W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR = 0, 1, 2, 3
+W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR, W_BF16 = 0, 1, 2, 3, 4
 A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
@@ -417,6 +417,11 @@ class MoELayer:
         fuse_route: plain top-k routing goes through moe_layer_forward (routing inside
         stage 1 where the batch allows); False keeps the separate calls."""
         self.E_local = w1.shape[0]
+        if wfmt == W_BF16:
+            if tiled:
+                raise ValueError("MoELayer: unquantised bf16 weights take the canonical layout only (tiled=False)")
+            if block_m is not None and block_m < 64:
+                raise ValueError(f"MoELayer: unquantised bf16 weights need block_m 64 or 128 (got {block_m})")
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
             w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
@@ -442,6 +447,8 @@ class MoELayer:
         key = (T, str(dev))
         if key not in self._bufs:
             bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total)
+            if self.wfmt == W_BF16:
+                bm = max(bm, 64)  # the bf16 weight path runs on the 64/128-row blocks only
             cap = moe_sort_capacity(T, self.K, self.E_local, bm)
             b = dict(
                 bm=bm,

@@ -92,7 +92,7 @@ __device__ __forceinline__ float ldf(const float* base, size_t off, bool ok) {
 
 template <int WF, int NT>
 struct WeightRegs {
-  i32x4 w[NT][WF == kWMxfp4 ? 1 : 2];  // 16 B (MXFP4) or 32 B (FP8) per tile
+  i32x4 w[NT][WF == kWMxfp4 ? 1 : (WF == kWBf16 ? 4 : 2)];  // 16 B (MXFP4), 32 B (FP8), 64 B (bf16) per tile
   uint32_t s[NT];                      // MXFP4: E8M0 byte
   float sb[NT];                        // FP8 block: w_scale of this chunk
 };
@@ -105,7 +105,7 @@ struct WeightRegs {
 template <int WF, int WL>
 struct WLayout {
   static constexpr size_t kBlock = (WF == kWMxfp4) ? 1088 : 2048;
-  static constexpr size_t kDataStride = WL ? kBlock : ((WF == kWMxfp4) ? 64 : 128);  // per 128-K chunk
+  static constexpr size_t kDataStride = WL ? kBlock : ((WF == kWMxfp4) ? 64 : (WF == kWBf16 ? 256 : 128));  // per 128-K chunk
   static constexpr size_t kScaleStride = WL ? kBlock : 4;
   static constexpr size_t kHiOff = WL ? 1024 : 16;  // FP8: second 16 B piece of the lane
   __device__ static const uint8_t* data(const GemmParams& p, int e, int trow, int li, int g, int lane, int K) {
@@ -113,8 +113,9 @@ struct WLayout {
       const size_t blk = ((size_t)e * p.Nw + trow) / 16 * (size_t)((K + 127) / 128);
       return p.w + blk * kBlock + 16 * lane;
     } else {
-      const size_t rowb = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
-      return p.w + ((size_t)e * p.Nw + trow + li) * rowb + (WF == kWMxfp4 ? 16 * g : 32 * g);
+      // bytes per row and per lane's 32 K elements: MXFP4 K/2 and 16, FP8 K and 32, bf16 2K and 64
+      const size_t rowb = (WF == kWMxfp4) ? (size_t)K / 2 : (WF == kWBf16 ? (size_t)K * 2 : (size_t)K);
+      return p.w + ((size_t)e * p.Nw + trow + li) * rowb + (WF == kWMxfp4 ? 16 * g : (WF == kWBf16 ? 64 * g : 32 * g));
     }
   }
   __device__ static const uint8_t* scale(const GemmParams& p, int e, int trow, int li, int g, int lane, int K) {
@@ -243,8 +244,8 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     col[t] = c;
     wrow[t] = trow + li;
     w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
-    ws_src[t] = WLay::scale(p, e, trow, li, g, lane, K);
-    wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk;
+    ws_src[t] = (WF == kWMxfp4) ? WLay::scale(p, e, trow, li, g, lane, K) : nullptr;
+    wsb_src[t] = (WF == kWFp8Block) ? (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk : nullptr;
     wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, trow + li)] : 1.0f;
   }
 
@@ -278,7 +279,10 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     const bool kok = c * 128 + 32 * g < K;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if constexpr (WF == kWMxfp4) {
+      if constexpr (WF == kWBf16) {  // the lane's 32 bf16 values, one 16 B piece per K-step of 8
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.w[t][q] = ld16(w_src[t], (size_t)c * WLay::kDataStride + 16 * q, kok);
+      } else if constexpr (WF == kWMxfp4) {
         r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
         r.s[t] = ld8(ws_src[t], (size_t)c * WLay::kScaleStride, kok);
       } else {
@@ -309,13 +313,18 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         for (int m = 0; m < MT; ++m) af[m] = *(const bf16x8*)(la + (m * 16 + li) * LROW + 64 * g + 16 * st);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const float sc = e8m0_to_f32(wr.s[t]);
-          const uint32_t dw = (uint32_t)wr.w[t][0][st];
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
-          const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          bf16x8 bfr;
+          if constexpr (WF == kWBf16) {  // unquantised: the loaded bf16 values as they are
+            bfr = __builtin_bit_cast(bf16x8, wr.w[t][st]);
+          } else {
+            const float sc = e8m0_to_f32(wr.s[t]);
+            const uint32_t dw = (uint32_t)wr.w[t][0][st];
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
+            bfr = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          }
 #pragma unroll
           for (int m = 0; m < MT; ++m)
             acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bfr, acc[m][t], 0, 0, 0);
@@ -1471,7 +1480,7 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
 }
 
 template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
-static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
+static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
     const size_t tile_lds = persist_lds_bytes(AF, p_in.K, MOE_PERSIST_WAVES);
     const bool bias = EPI && p_in.bias;
@@ -1494,7 +1503,8 @@ static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   }
   if (p_in.route) return hipErrorInvalidValue;  // the fused route + sort runs in the persistent kernel only
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
-  constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : 4;
+  // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
+  constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : (WF == kWBf16 ? 2 : 4);
   constexpr int COLS_PER_WG = kSplit ? ((STAGE == 1) ? 8 * NT : 16 * NT) : ((STAGE == 1) ? 32 * NT : 64 * NT);
   GemmParams p = p_in;
   const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
@@ -1515,6 +1525,16 @@ static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
   else
     moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
+static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
+  // bf16 weights: canonical layout, 64/128-row kernel only (the ABI enforces both)
+  if constexpr (WF == kWBf16 && (BM < 64 || WL != 0)) {
+    return hipErrorInvalidValue;
+  } else {
+    return launch_one_impl<STAGE, WF, AF, BM, WL, EPI>(p_in, stream);
+  }
 }
 
 template <int STAGE, int WF, int AF, int WL, int EPI>
@@ -1546,6 +1566,7 @@ static hipError_t launch_stage(int wfmt, int afmt, int bm, const GemmParams& p, 
   if (wfmt == kWFp8Channel && afmt == kAFp8Token) return launch_bm<STAGE, kWFp8Channel, kAFp8Token>(bm, p, stream);
   // per tensor: the per-channel kernels with scale strides 0 (GemmParams::wsc_rs, asc_rs)
   if (wfmt == kWFp8Tensor && afmt == kAFp8Tensor) return launch_bm<STAGE, kWFp8Channel, kAFp8Token>(bm, p, stream);
+  if (wfmt == kWBf16 && afmt == kABf16) return launch_bm<STAGE, kWBf16, kABf16>(bm, p, stream);
   return hipErrorInvalidValue;
 }
 

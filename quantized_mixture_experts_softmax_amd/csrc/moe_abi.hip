@@ -58,7 +58,7 @@ size_t scale_bytes(int f, size_t rows, size_t cols) {
 bool pair_supported(int wf, int af) {
   return (wf == MOE_W_MXFP4 && (af == MOE_A_BF16 || af == MOE_A_MXFP4_G32)) ||
          (wf == MOE_W_FP8_BLOCK128 && af == MOE_A_FP8_G128) || (wf == MOE_W_FP8_CHANNEL && af == MOE_A_FP8_TOKEN) ||
-         (wf == MOE_W_FP8_TENSOR && af == MOE_A_FP8_TENSOR);
+         (wf == MOE_W_FP8_TENSOR && af == MOE_A_FP8_TENSOR) || (wf == MOE_W_BF16 && af == MOE_A_BF16);
 }
 
 moe_status check_shapes(const moe_forward_args* a) {
@@ -81,13 +81,17 @@ moe_status check_shapes(const moe_forward_args* a) {
     return fail(MOE_EINVAL, "the router weight goes on the input only with one slot per token (K = %d)", a->K);
   if (a->gate_up_interleaved && a->wfmt == MOE_W_FP8_BLOCK128)
     return fail(MOE_EUNSUPPORTED, "interleaved gate/up rows would split FP8 128x128 scale blocks");
-  if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_FP8_TENSOR) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
+  if (a->wfmt < MOE_W_MXFP4 || a->wfmt > MOE_W_BF16) return fail(MOE_EINVAL, "unknown weight format %d", (int)a->wfmt);
   if (a->afmt < MOE_A_BF16 || a->afmt > MOE_A_FP8_TENSOR) return fail(MOE_EINVAL, "unknown activation format %d", (int)a->afmt);
   if (!pair_supported(a->wfmt, a->afmt))
     return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)a->wfmt,
                 (int)a->afmt);
   if (a->weight_layout != MOE_LAYOUT_CANONICAL && a->weight_layout != MOE_LAYOUT_TILED)
     return fail(MOE_EINVAL, "unknown weight layout %d", (int)a->weight_layout);
+  if (a->wfmt == MOE_W_BF16 && a->weight_layout != MOE_LAYOUT_CANONICAL)
+    return fail(MOE_EUNSUPPORTED, "bf16 weights use the canonical layout");
+  if (a->wfmt == MOE_W_BF16 && a->block_m < 64)
+    return fail(MOE_EUNSUPPORTED, "bf16 weights run on 64- or 128-row blocks (block_m %d)", a->block_m);
   return ok();
 }
 
@@ -129,7 +133,7 @@ moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w
 moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I) {
   if (act != MOE_ACT_SILU && act != MOE_ACT_SWIGLU_OAI)
     return fail(MOE_EUNSUPPORTED, "activation %d is not implemented (SiLU-and-mul, SwiGLU-OAI)", (int)act);
-  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_FP8_TENSOR) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
+  if (wfmt < MOE_W_MXFP4 || wfmt > MOE_W_BF16) return fail(MOE_EINVAL, "unknown weight format %d", (int)wfmt);
   if (afmt < MOE_A_BF16 || afmt > MOE_A_FP8_TENSOR) return fail(MOE_EINVAL, "unknown activation format %d", (int)afmt);
   if (!pair_supported(wfmt, afmt))
     return fail(MOE_EUNSUPPORTED, "weight format %d with activation format %d is not implemented", (int)wfmt, (int)afmt);
@@ -335,7 +339,8 @@ moe_status experts_forward(const moe_forward_args* a, const FusedRoute* r, hipSt
   if (st != MOE_OK) return st;
   if (a->T == 0) return ok();
   // tiled MXFP4 weights carry their scales inside the blocks
-  const bool scales_needed = !(a->wfmt == MOE_W_MXFP4 && a->weight_layout == MOE_LAYOUT_TILED);
+  const bool scales_needed =
+      !(a->wfmt == MOE_W_MXFP4 && a->weight_layout == MOE_LAYOUT_TILED) && a->wfmt != MOE_W_BF16;
   if (!a->hidden_states || !a->w1 || !a->w2 || (scales_needed && (!a->w1_scale || !a->w2_scale)) || !a->topk_ids ||
       !a->topk_weights || !a->sorted_slots || !a->block_expert || !a->num_padded || !a->out)
     return fail(MOE_EINVAL, "moe_experts_forward: NULL pointer");

@@ -11,7 +11,7 @@ namespace moe {
 enum { kABf16 = 0, kAMxfp4 = 1, kAFp8G128 = 2, kAFp8Token = 3, kAFp8Tensor = 4 };
 // Weight formats (values match moe_wfmt).  kWFp8Tensor runs as kWFp8Channel with scale
 // strides (expert 1, row 0).
-enum { kWMxfp4 = 0, kWFp8Block = 1, kWFp8Channel = 2, kWFp8Tensor = 3 };
+enum { kWMxfp4 = 0, kWFp8Block = 1, kWFp8Channel = 2, kWFp8Tensor = 3, kWBf16 = 4 };
 
 // One grouped-GEMM launch over the padded sorted rows.
 struct GemmParams {

@@ -62,7 +62,12 @@ def act_dev(act: dict | None) -> dict | None:
 
 
 def dev_weights(data: dict) -> dict:
-    return {k: to_dev(data[k]) for k in ("w1", "w1_scale", "w2", "w2_scale")}
+    """The weights and scales on the GPU (bf16 weights as bf16 tensors; absent scales None)."""
+    out = {}
+    for k in ("w1", "w1_scale", "w2", "w2_scale"):
+        a = data[k]
+        out[k] = None if a is None else (bf16_dev(a) if a.dtype == np.uint16 else to_dev(a))
+    return out
 
 
 def score_name(w: synth.Workload) -> str:

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from quantized_mixture_experts_softmax_amd import binding as B
 
@@ -187,3 +188,35 @@ def test_layer_forward_rejects(lib):
     assert f(_args(), *route_with(5, None)) == B.MOE_EINVAL                 # expert_counts NULL
     assert f(_args(), *route_with(0, P(FAKE + 2))) == B.MOE_EINVAL          # misaligned logits
     assert f(_args(K=3, E_total=2), *ok_route) == B.MOE_EINVAL              # topk > routed experts
+
+
+def test_bf16_weight_rejects(lib):
+    """Unquantised bf16 weights run with bf16 activations on 64/128-row blocks over the
+    canonical layout; every other combination is refused on the host."""
+    fwd = lambda a: lib.moe_experts_forward(ctypes.byref(a), None)
+    bf = dict(wfmt=B.W_BF16, afmt=B.A_BF16, w1_scale=None, w2_scale=None)
+    for bm in (16, 32):
+        assert fwd(_args(block_m=bm, **bf)) == B.MOE_EUNSUPPORTED
+        assert "row blocks" in B.moe_last_error()
+    assert fwd(_args(block_m=64, weight_layout=B.LAYOUT_TILED, **bf)) == B.MOE_EUNSUPPORTED
+    assert "canonical" in B.moe_last_error()
+    assert fwd(_args(block_m=64, **dict(bf, afmt=B.A_MXFP4_G32))) == B.MOE_EUNSUPPORTED
+    assert fwd(_args(block_m=64, wfmt=5, afmt=B.A_BF16)) == B.MOE_EINVAL
+    assert fwd(_args(block_m=64, workspace_bytes=16, **bf)) == B.MOE_EWORKSPACE  # valid up to the workspace
+    assert lib.moe_supports(B.W_BF16, B.A_BF16, 0, 2880, 2880) == B.MOE_OK
+    assert lib.moe_supports(B.W_BF16, B.A_FP8_TOKEN, 0, 2880, 2880) == B.MOE_EUNSUPPORTED
+    assert lib.moe_tiled_weight_bytes(B.W_BF16, 2, 64, 256) == 0
+    P = ctypes.c_void_p
+    assert lib.moe_tile_weights(B.W_BF16, 2, 32, 64, P(FAKE), None, P(FAKE), None) == B.MOE_EINVAL
+
+
+def test_bf16_layer_rejects_on_host():
+    """MoELayer refuses the tiled layout and blocks under 64 rows for bf16 weights
+    before it touches a device."""
+    w1 = torch.zeros((2, 64, 64), dtype=torch.bfloat16)
+    w2 = torch.zeros((2, 64, 32), dtype=torch.bfloat16)
+    kw = dict(H=64, I=32, E=2, topk=1, wfmt=B.W_BF16, afmt=B.A_BF16)
+    with pytest.raises(ValueError, match="canonical"):
+        B.MoELayer(w1, None, w2, None, tiled=True, **kw)
+    with pytest.raises(ValueError, match="block_m"):
+        B.MoELayer(w1, None, w2, None, block_m=32, **kw)
