@@ -47,6 +47,9 @@ constexpr int kXcds = 8;
 #ifndef MOE_KSPLIT_NT_BF16
 #define MOE_KSPLIT_NT_BF16 8
 #endif
+#ifndef MOE_SCALE_DWORD
+#define MOE_SCALE_DWORD 1
+#endif
 #ifndef MOE_KSPLIT_NT_Q
 #define MOE_KSPLIT_NT_Q 4
 #endif
@@ -94,6 +97,7 @@ template <int WF, int NT>
 struct WeightRegs {
   i32x4 w[NT][WF == kWMxfp4 ? 1 : (WF == kWBf16 ? 4 : 2)];  // 16 B (MXFP4), 32 B (FP8), 64 B (bf16) per tile
   uint32_t s[NT];                      // MXFP4: E8M0 byte
+  uint32_t s4;                         // tiled MXFP4 (64/128-row kernel): 4 scale bytes, see kScaleDword
   float sb[NT];                        // FP8 block: w_scale of this chunk
 };
 
@@ -248,6 +252,24 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     wsb_src[t] = (WF == kWFp8Block) ? (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk : nullptr;
     wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, trow + li)] : 1.0f;
   }
+  // Tiled MXFP4 with MXFP4 activations: a lane's E8M0 byte for tile t is byte `lane` of
+  // the 64-byte scale part of tile t's block.  One dword load per lane fetches the scales
+  // of all four tiles of a chunk (lane l reads bytes [4 (l % 16), +4) of tile l / 16) in
+  // place of a byte load per tile; each lane then takes its byte from lane 16 t + l / 4
+  // with ds_bpermute.  On large w4a4 batches the vector-memory return path (TD), not HBM
+  // or MFMA, bounds this kernel, and a byte load costs it about half a 16-byte one
+  // (counters on MI355X); the step gained 6%.  w4a16, whose LDS pipe carries four times
+  // the A reads, lost 9% with it and keeps the byte loads.
+  constexpr bool kScaleDword = (WF == kWMxfp4) && (AF == kAMxfp4) && (WL != 0) && (MOE_SCALE_DWORD != 0);
+  static_assert(!kScaleDword || NT <= 4, "one dword per lane holds the scales of four tiles");
+  const uint8_t* ws4_src = nullptr;
+  if constexpr (kScaleDword) {
+    const int tt = (lane >> 4) % NT;
+    const uint8_t* b = ws_src[0];
+#pragma unroll
+    for (int t = 1; t < NT; ++t) b = (tt == t) ? ws_src[t] : b;
+    ws4_src = b - lane + 4 * (lane & 15);
+  }
 
   auto load_a = [&](int c, i32x4 (&reg)[AIT]) {
 #pragma unroll
@@ -284,12 +306,23 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         for (int q = 0; q < 4; ++q) r.w[t][q] = ld16(w_src[t], (size_t)c * WLay::kDataStride + 16 * q, kok);
       } else if constexpr (WF == kWMxfp4) {
         r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
-        r.s[t] = ld8(ws_src[t], (size_t)c * WLay::kScaleStride, kok);
+        if constexpr (!kScaleDword) r.s[t] = ld8(ws_src[t], (size_t)c * WLay::kScaleStride, kok);
       } else {
         r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
         r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)c * WLay::kDataStride + WLay::kHiOff, kok);
         if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)(c < nch ? c : 0), c < nch);
       }
+    }
+    // (the tail chunk's block holds zero scale bytes past K; chunks past the end read the zero page)
+    if constexpr (kScaleDword) r.s4 = ld_global<uint32_t>(ws4_src, (size_t)c * WLay::kScaleStride, c < nch);
+  };
+  // the E8M0 byte of tile t for this lane
+  auto wscale = [&](const WeightRegs<WF, NT>& wr, int t) -> uint32_t {
+    if constexpr (kScaleDword) {
+      const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * t + (lane >> 2)) << 2, (int)wr.s4);
+      return (v >> (8 * (lane & 3))) & 0xFFu;
+    } else {
+      return wr.s[t];
     }
   };
 
@@ -304,6 +337,11 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   // MFMAs of one chunk: A from LDS buffer buf, weights wr
   auto compute = [&](int buf, const WeightRegs<WF, NT>& wr) {
     const uint8_t* la = lds_a[buf];
+    uint32_t wsb[NT] = {};
+    if constexpr (WF == kWMxfp4) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wsb[t] = wscale(wr, t);
+    }
     if constexpr (AF == kABf16) {
       // w4a16: fp4 -> bf16 in registers, 4 K-steps of 8 per chunk
 #pragma unroll
@@ -317,7 +355,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
           if constexpr (WF == kWBf16) {  // unquantised: the loaded bf16 values as they are
             bfr = __builtin_bit_cast(bf16x8, wr.w[t][st]);
           } else {
-            const float sc = e8m0_to_f32(wr.s[t]);
+            const float sc = e8m0_to_f32(wsb[t]);
             const uint32_t dw = (uint32_t)wr.w[t][0][st];
             const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
             const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
@@ -341,7 +379,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         for (int t = 0; t < NT; ++t) {
           const i32x8 b8 = {wr.w[t][0][0], wr.w[t][0][1], wr.w[t][0][2], wr.w[t][0][3], 0, 0, 0, 0};
           acc[m][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[m][t], 4, 4, 0, sa, 0,
-                                                                        (int)wr.s[t]);
+                                                                        (int)wsb[t]);
         }
       }
     } else {
