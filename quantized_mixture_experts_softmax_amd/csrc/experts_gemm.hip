@@ -92,6 +92,12 @@ __device__ __forceinline__ uint32_t ld8(const uint8_t* base, size_t off, bool ok
 __device__ __forceinline__ float ldf(const float* base, size_t off, bool ok) {
   return ld_global<float>(base, off * sizeof(float), ok);
 }
+// A read-only fp32 at a wave-uniform address through the scalar data cache (a load from
+// the constant address space; the cache is invalidated at each dispatch and nothing in the
+// kernel writes the data).
+__device__ __forceinline__ float ld_uniform_f32(const float* ptr) {
+  return *(const __attribute__((address_space(4))) float*)ptr;
+}
 
 template <int WF, int NT>
 struct WeightRegs {
@@ -170,7 +176,8 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   const int e = p.block_expert[b];
   if (e < 0) return;
 
-  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile rows and block scales stay scalar
   const int K = p.K, nch = (K + 127) / 128;
   const int TK = p.T * p.slots_per_token;
   const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
@@ -222,6 +229,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   float wsc[NT];
   int col[NT], wrow[NT];
   bool col_ok[NT];
+  const int cb_u = nt_idx * COLS_PER_WG + w * (NT / 2) * 16;  // stage 1: the wave's first output column
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int c, trow;
@@ -249,7 +257,15 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     wrow[t] = trow + li;
     w_src[t] = WLay::data(p, e, trow, li, g, lane, K);
     ws_src[t] = (WF == kWMxfp4) ? WLay::scale(p, e, trow, li, g, lane, K) : nullptr;
-    wsb_src[t] = (WF == kWFp8Block) ? (const float*)p.w_scale + ((size_t)e * nbn + trow / 128) * nbk : nullptr;
+    if constexpr (WF == kWFp8Block) {
+      // the tile's first weight row, from wave-uniform values only (trow is 0 in the lanes
+      // past N), so the block scale is one scalar load per chunk, not a vector load
+      const int c0 = (STAGE == 1) ? cb_u + (t % (NT / 2)) * 16 : nt_idx * COLS_PER_WG + w * NT * 16 + t * 16;
+      const int r0 = c0 < p.N ? ((STAGE == 1 && t >= NT / 2) ? p.N + c0 : c0) : 0;
+      wsb_src[t] = (const float*)p.w_scale + ((size_t)e * nbn + r0 / 128) * nbk;
+    } else {
+      wsb_src[t] = nullptr;
+    }
     wsc[t] = (WF == kWFp8Channel) ? ((const float*)p.w_scale)[wsc_index(p, e, trow + li)] : 1.0f;
   }
   // Tiled MXFP4 with MXFP4 activations: a lane's E8M0 byte for tile t is byte `lane` of
@@ -310,7 +326,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       } else {
         r.w[t][0] = ld16(w_src[t], (size_t)c * WLay::kDataStride, kok);
         r.w[t][WF == kWMxfp4 ? 0 : 1] = ld16(w_src[t], (size_t)c * WLay::kDataStride + WLay::kHiOff, kok);
-        if constexpr (WF == kWFp8Block) r.sb[t] = ldf(wsb_src[t], (size_t)(c < nch ? c : 0), c < nch);
+        if constexpr (WF == kWFp8Block) r.sb[t] = ld_uniform_f32(wsb_src[t] + (c < nch ? c : 0));
       }
     }
     // (the tail chunk's block holds zero scale bytes past K; chunks past the end read the zero page)
