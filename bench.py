@@ -214,8 +214,8 @@ def main() -> int:
 
     if args.layout is None:
         args.layout = "canonical" if w.wfmt == synth.W_BF16 else "tiled"
-    if w.wfmt == synth.W_BF16 and (args.layout == "tiled" or (args.block_m or 64) < 64):
-        print("bench.py: bf16 weights run on the canonical layout with 64- or 128-row blocks", file=sys.stderr)
+    if w.wfmt == synth.W_BF16 and (args.layout == "tiled" or args.block_m == 32):
+        print("bench.py: bf16 weights run on the canonical layout with 16-, 64- or 128-row blocks", file=sys.stderr)
         return 2
     grouped = None
     if args.router == "grouped":

@@ -57,7 +57,8 @@ typedef enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scor
  *                      w1_scale [E], w2_scale [E]  ([rocm_aiter_moe] AiterFp8TensorExperts)
  *   MOE_W_BF16         unquantised: w1 bf16 [E, 2I, H], w2 bf16 [E, H, I], no scales (pass
  *                      NULL); with MOE_A_BF16 only, the canonical layout only, and block_m
- *                      64 or 128  ([rocm_aiter_moe] AiterUnquantizedExperts)
+ *                      64 or 128, or 16 when H, I <= 2944 (the 16-row activation tile is
+ *                      kept in LDS)  ([rocm_aiter_moe] AiterUnquantizedExperts)
  * In w1 rows [0, I) are the gate projection and rows [I, 2I) the up projection. */
 typedef enum moe_wfmt {
   MOE_W_MXFP4 = 0, MOE_W_FP8_BLOCK128 = 1, MOE_W_FP8_CHANNEL = 2, MOE_W_FP8_TENSOR = 3, MOE_W_BF16 = 4
@@ -259,7 +260,7 @@ moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
  * Limits: H % 32 == 0, I % 32 == 0, H, I <= 65536, 1 <= K <= 64, E_total <= 1024,
  * block_m in {16, 32, 64, 128}; (wfmt, afmt) one of
  *   (MXFP4, BF16) (MXFP4, MXFP4_G32) (FP8_BLOCK128, FP8_G128) (FP8_CHANNEL, FP8_TOKEN)
- *   (FP8_TENSOR, FP8_TENSOR) (BF16, BF16: block_m 64 or 128, canonical layout)
+ *   (FP8_TENSOR, FP8_TENSOR) (BF16, BF16: canonical layout; block_m 64, 128, or 16 with H, I <= 2944)
  * (others: MOE_EUNSUPPORTED).  Pointers to 16-byte aligned memory.
  * ---------------------------------------------------------------------------------- */
 typedef struct moe_forward_args {

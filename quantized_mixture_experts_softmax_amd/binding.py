@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 SCORE = {"softmax": 0, "sigmoid": 1}
 W_MXFP4, W_FP8_BLOCK128, W_FP8_CHANNEL, W_FP8_TENSOR, W_BF16 = 0, 1, 2, 3, 4
+# bf16 weights on 16-row blocks: the persistent kernel's activation tile (16 x K bf16) must fit
+# its LDS, i.e. at most 23 chunks of 128 (moe_experts_forward refuses larger H or I there)
+BF16_SMALL_BLOCK_MAX_K = 2944
 A_BF16, A_MXFP4_G32, A_FP8_G128, A_FP8_TOKEN, A_FP8_TENSOR = 0, 1, 2, 3, 4
 ACT_SILU, ACT_SWIGLU_OAI = 0, 1
 
@@ -420,8 +423,9 @@ class MoELayer:
         if wfmt == W_BF16:
             if tiled:
                 raise ValueError("MoELayer: unquantised bf16 weights take the canonical layout only (tiled=False)")
-            if block_m is not None and block_m < 64:
-                raise ValueError(f"MoELayer: unquantised bf16 weights need block_m 64 or 128 (got {block_m})")
+            if block_m == 32 or (block_m == 16 and max(H, I) > BF16_SMALL_BLOCK_MAX_K):
+                raise ValueError(f"MoELayer: unquantised bf16 weights take block_m 16 (H, I <= "
+                                 f"{BF16_SMALL_BLOCK_MAX_K}), 64 or 128 (got {block_m})")
         self.weight_layout = LAYOUT_TILED if tiled else LAYOUT_CANONICAL
         if tiled:
             w1 = moe_tile_weights(w1, w1_scale, wfmt, H)
@@ -447,8 +451,8 @@ class MoELayer:
         key = (T, str(dev))
         if key not in self._bufs:
             bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total)
-            if self.wfmt == W_BF16:
-                bm = max(bm, 64)  # the bf16 weight path runs on the 64/128-row blocks only
+            if self.wfmt == W_BF16 and (bm == 32 or (bm == 16 and max(self.H, self.I) > BF16_SMALL_BLOCK_MAX_K)):
+                bm = 64  # bf16 weights: no 32-row kernel; 16-row blocks only with the activation tile in LDS
             cap = moe_sort_capacity(T, self.K, self.E_local, bm)
             b = dict(
                 bm=bm,

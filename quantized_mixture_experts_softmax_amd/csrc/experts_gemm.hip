@@ -995,8 +995,10 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
   constexpr int BM = 16, NT = 2;
   constexpr int SEG = a_units_per_chunk(AF);
   // vector-memory instructions of one ring step (load_next): per tile, the 16 B code
-  // piece(s) and the E8M0 byte (MXFP4) or the fp32 block / channel scale (FP8)
-  constexpr int kStepLoads = NT * (WF == kWMxfp4 ? 2 : 3);
+  // piece(s) and the E8M0 byte (MXFP4) or the fp32 block / channel scale (FP8), or the
+  // four 16 B pieces of 32 bf16 values (bf16 weights)
+  constexpr int kStepLoads = NT * (WF == kWMxfp4 ? 2 : (WF == kWBf16 ? 4 : 3));
+  static_assert(WF != kWBf16 || (AF == kABf16 && WL == 0), "bf16 weights: bf16 activations, canonical layout");
   constexpr int kRingLoads = D * kStepLoads;
   static_assert(kRingLoads <= 63, "vmcnt range");
   constexpr int kThreads = 64 * WAVES;
@@ -1088,7 +1090,10 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
         const int trow = tok ? trow_of(lu, t) : 0;  // the K-tail check is per lane; the block scale is not
         const uint8_t* src = WLay::data(p, e, trow, li, g, lane, K);
         r.w[t][0] = ld16(src, (size_t)lc * WLay::kDataStride, ok);
-        if constexpr (WF == kWMxfp4) {
+        if constexpr (WF == kWBf16) {
+#pragma unroll
+          for (int q = 1; q < 4; ++q) r.w[t][q] = ld16(src, (size_t)lc * WLay::kDataStride + 16 * q, ok);
+        } else if constexpr (WF == kWMxfp4) {
           r.s[t] = ld8(WLay::scale(p, e, trow, li, g, lane, K), (size_t)lc * WLay::kScaleStride, ok);
         } else {
           r.w[t][1] = ld16(src, (size_t)lc * WLay::kDataStride + WLay::kHiOff, ok);
@@ -1209,13 +1214,18 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
           const bf16x8 af = *(const bf16x8*)(arow + 16 * ((4 * g + st) ^ swz));
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const float sc = e8m0_to_f32(wr.s[t]);
-            const uint32_t dw = (uint32_t)wr.w[t][0][st];
-            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
-            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
-            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
-            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
-            const bf16x8 bfr = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            bf16x8 bfr;
+            if constexpr (WF == kWBf16) {  // unquantised: the loaded bf16 values as they are
+              bfr = __builtin_bit_cast(bf16x8, wr.w[t][st]);
+            } else {
+              const float sc = e8m0_to_f32(wr.s[t]);
+              const uint32_t dw = (uint32_t)wr.w[t][0][st];
+              const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0);
+              const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1);
+              const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2);
+              const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3);
+              bfr = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            }
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[t], 0, 0, 0);
           }
         }
@@ -1432,6 +1442,9 @@ constexpr size_t kPersistLdsFusedMax = 160 * 1024;
 #ifndef MOE_PERSIST_WAVES
 #define MOE_PERSIST_WAVES 16
 #endif
+#ifndef MOE_PERSIST_DEPTH_BF16  // bf16 weights: 128 B per lane and step already; depth 1 measured
+#define MOE_PERSIST_DEPTH_BF16 1   // best on the decode shape (2 -5%, 3 -18%, 4 -37%)
+#endif
 #ifndef MOE_PERSIST_DEPTH_F4
 #define MOE_PERSIST_DEPTH_F4 6
 #endif
@@ -1502,6 +1515,11 @@ static bool route_stage1_lds(int afmt, int K_dim, int N, bool bias, int T, int E
   return all <= persist_lds_limit();
 }
 
+bool persist_launch_fits(int afmt, int stage, int K_dim, int N, bool bias) {
+  const size_t tile = persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES);
+  return tile <= kPersistLdsMax && tile + (bias ? bias_slice_bytes(stage, N) : 0) <= persist_lds_limit();
+}
+
 bool route_stage1_fusable(int afmt, int K_dim, int N, int T, int E, int topk, int n_shared, bool bias) {
   size_t off = 0, all = 0;
   return T > 0 && persist_lds_bytes(afmt, K_dim, MOE_PERSIST_WAVES) <= kPersistLdsMax &&
@@ -1512,7 +1530,8 @@ template <int STAGE, int WF, int AF, int WL, int EPI, int RS>
 static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t stream) {
   constexpr int WAVES = MOE_PERSIST_WAVES;
   constexpr int D = (WF == kWMxfp4) ? (AF == kAMxfp4 ? MOE_PERSIST_DEPTH_F4A4 : MOE_PERSIST_DEPTH_F4)
-                                    : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8);
+                                    : (WF == kWBf16 ? MOE_PERSIST_DEPTH_BF16
+                                                    : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8));
   if (p.num_blocks == 0) return hipSuccess;
   auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI, RS>;
   static bool attr_set = false;
@@ -1557,6 +1576,9 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   }
   if (p_in.route) return hipErrorInvalidValue;  // the fused route + sort runs in the persistent kernel only
   constexpr bool kSplit = BM <= 32;  // small blocks: K split over waves, no LDS staging
+  if constexpr (WF == kWBf16 && kSplit) {
+    return hipErrorInvalidValue;  // bf16 weights: the persistent kernel or 64/128-row blocks only
+  } else {
   // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : (WF == kWBf16 ? 2 : 4);
   constexpr int COLS_PER_WG = kSplit ? ((STAGE == 1) ? 8 * NT : 16 * NT) : ((STAGE == 1) ? 32 * NT : 64 * NT);
@@ -1579,12 +1601,14 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   else
     moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
   return hipGetLastError();
+  }
 }
 
 template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
 static hipError_t launch_one(const GemmParams& p_in, hipStream_t stream) {
-  // bf16 weights: canonical layout, 64/128-row kernel only (the ABI enforces both)
-  if constexpr (WF == kWBf16 && (BM < 64 || WL != 0)) {
+  // bf16 weights: canonical layout; 16-row blocks on the persistent kernel (activation
+  // tile in LDS) or 64/128-row blocks (the ABI enforces all three)
+  if constexpr (WF == kWBf16 && (BM == 32 || WL != 0)) {
     return hipErrorInvalidValue;
   } else {
     return launch_one_impl<STAGE, WF, AF, BM, WL, EPI>(p_in, stream);

@@ -90,8 +90,12 @@ moe_status check_shapes(const moe_forward_args* a) {
     return fail(MOE_EINVAL, "unknown weight layout %d", (int)a->weight_layout);
   if (a->wfmt == MOE_W_BF16 && a->weight_layout != MOE_LAYOUT_CANONICAL)
     return fail(MOE_EUNSUPPORTED, "bf16 weights use the canonical layout");
-  if (a->wfmt == MOE_W_BF16 && a->block_m < 64)
-    return fail(MOE_EUNSUPPORTED, "bf16 weights run on 64- or 128-row blocks (block_m %d)", a->block_m);
+  if (a->wfmt == MOE_W_BF16 && a->block_m == 32)
+    return fail(MOE_EUNSUPPORTED, "bf16 weights run on 16-, 64- or 128-row blocks (block_m %d)", a->block_m);
+  if (a->wfmt == MOE_W_BF16 && a->block_m == 16 &&
+      !(moe::persist_launch_fits(moe::kABf16, 1, a->H, 2 * a->I, a->w1_bias != nullptr) &&
+        moe::persist_launch_fits(moe::kABf16, 2, a->I, a->H, a->w2_bias != nullptr)))
+    return fail(MOE_EUNSUPPORTED, "bf16 weights on 16-row blocks need H, I <= 2944 (the activation tile in LDS)");
   return ok();
 }
 

@@ -107,6 +107,9 @@ bool route_sort_fusable(int T, int E, int K);
 // Whether stage 1 can run with the router + sort fused in (16-row blocks, the persistent
 // kernel, LDS for the tile, the bias slice, the route scratch and the kept tables); K_dim
 // = H, N = I, T tokens, E routed experts, topk, n_shared, bias: w1 biases present.
+// Whether 16-row blocks of this activation format run on the persistent kernel for one
+// stage (K_dim: the GEMM's K; N: its output columns; bias: the stage has a bias slice).
+bool persist_launch_fits(int afmt, int stage, int K_dim, int N, bool bias);
 bool route_stage1_fusable(int afmt, int K_dim, int N, int T, int E, int topk, int n_shared, bool bias);
 hipError_t launch_route_sort(const float* logits, int T, int E, int topk, int score, int renorm, int n_shared,
                              float shared_w, int bm, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,

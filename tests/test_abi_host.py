@@ -191,13 +191,17 @@ def test_layer_forward_rejects(lib):
 
 
 def test_bf16_weight_rejects(lib):
-    """Unquantised bf16 weights run with bf16 activations on 64/128-row blocks over the
-    canonical layout; every other combination is refused on the host."""
+    """Unquantised bf16 weights run with bf16 activations over the canonical layout on
+    64/128-row blocks, or on 16-row blocks while H, I <= 2944; every other combination is
+    refused on the host."""
     fwd = lambda a: lib.moe_experts_forward(ctypes.byref(a), None)
     bf = dict(wfmt=B.W_BF16, afmt=B.A_BF16, w1_scale=None, w2_scale=None)
-    for bm in (16, 32):
-        assert fwd(_args(block_m=bm, **bf)) == B.MOE_EUNSUPPORTED
-        assert "row blocks" in B.moe_last_error()
+    assert fwd(_args(block_m=32, **bf)) == B.MOE_EUNSUPPORTED
+    assert "row blocks" in B.moe_last_error()
+    assert fwd(_args(block_m=16, H=4096, **bf)) == B.MOE_EUNSUPPORTED
+    assert "2944" in B.moe_last_error()
+    assert fwd(_args(block_m=16, I=3072, **bf)) == B.MOE_EUNSUPPORTED
+    assert fwd(_args(block_m=16, workspace_bytes=16, **bf)) == B.MOE_EWORKSPACE  # H = I = 256: valid
     assert fwd(_args(block_m=64, weight_layout=B.LAYOUT_TILED, **bf)) == B.MOE_EUNSUPPORTED
     assert "canonical" in B.moe_last_error()
     assert fwd(_args(block_m=64, **dict(bf, afmt=B.A_MXFP4_G32))) == B.MOE_EUNSUPPORTED
@@ -211,8 +215,8 @@ def test_bf16_weight_rejects(lib):
 
 
 def test_bf16_layer_rejects_on_host():
-    """MoELayer refuses the tiled layout and blocks under 64 rows for bf16 weights
-    before it touches a device."""
+    """MoELayer refuses the tiled layout, 32-row blocks and 16-row blocks past H, I = 2944
+    for bf16 weights before it touches a device."""
     w1 = torch.zeros((2, 64, 64), dtype=torch.bfloat16)
     w2 = torch.zeros((2, 64, 32), dtype=torch.bfloat16)
     kw = dict(H=64, I=32, E=2, topk=1, wfmt=B.W_BF16, afmt=B.A_BF16)
@@ -220,3 +224,7 @@ def test_bf16_layer_rejects_on_host():
         B.MoELayer(w1, None, w2, None, tiled=True, **kw)
     with pytest.raises(ValueError, match="block_m"):
         B.MoELayer(w1, None, w2, None, block_m=32, **kw)
+    big = dict(kw, H=3072)
+    with pytest.raises(ValueError, match="block_m"):
+        B.MoELayer(torch.zeros((2, 64, 3072), dtype=torch.bfloat16), None,
+                   torch.zeros((2, 3072, 32), dtype=torch.bfloat16), None, block_m=16, **big)

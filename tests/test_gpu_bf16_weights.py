@@ -1,5 +1,5 @@
-"""GPU parity of the unquantised bf16 expert layer (bf16 weights and activations, the
-64/128-row kernel over the canonical layout) against the oracle, under the output
+"""GPU parity of the unquantised bf16 expert layer (bf16 weights and activations over the
+canonical layout; the persistent 16-row kernel and the 64/128-row kernel) against the oracle, under the output
 bound of the quantised paths: max|gpu - oracle| <= 2e-2 * rms and per-token relative
 L2 <= 1e-2 on the fp32 result, the bf16 output its round-to-nearest-even bit for bit.
 """
@@ -28,6 +28,11 @@ def _no_scales_oai(w, data, interleaved, bias, kind=1):
 
 CASES = [
     # name, workload, block_m
+    ("ragged-bm16", lambda: small(BF, T=40, H=320, I=288, E=6, k=2, seed=51), 16),
+    ("shared-sigmoid-bm16", lambda: small(BF, T=50, H=352, I=416, E=5, k=3, n_shared=1,
+                                          score=synth.SCORE_SIGMOID, seed=52), 16),
+    ("single-token-bm16", lambda: small(BF, T=1, H=256, I=160, E=4, k=2, seed=53), 16),
+    ("max-K-bm16", lambda: small(BF, T=20, H=2944, I=2944, E=3, k=2, seed=58), 16),
     ("ragged-bm64", lambda: small(BF, T=40, H=320, I=288, E=6, k=2, seed=51), 64),
     ("ragged-bm128", lambda: small(BF, T=40, H=320, I=288, E=6, k=2, seed=51), 128),
     ("shared-sigmoid-bm64", lambda: small(BF, T=50, H=352, I=416, E=5, k=3, n_shared=1,
@@ -48,8 +53,8 @@ def test_bf16_small(name, make, bm):
     full_check(w, data, res, what=f"bf16/{name}")
 
 
-@pytest.mark.parametrize("bm,itl,bias,kind", [(64, True, True, 1), (128, True, True, 1), (64, False, True, 0),
-                                              (128, False, False, 1)])
+@pytest.mark.parametrize("bm,itl,bias,kind", [(16, True, True, 1), (16, False, True, 0), (64, True, True, 1),
+                                              (128, True, True, 1), (64, False, True, 0), (128, False, False, 1)])
 def test_bf16_act_bias(bm, itl, bias, kind):
     w = small(BF, T=45, H=320, I=288, E=8, k=2, seed=55)
     data = synth.make_all(w)
@@ -60,22 +65,24 @@ def test_bf16_act_bias(bm, itl, bias, kind):
     full_check(w, data, res, what=what, act=act)
 
 
-def test_bf16_router_weight_on_input():
+@pytest.mark.parametrize("bm", [16, 64])
+def test_bf16_router_weight_on_input(bm):
     w = small(BF, T=40, H=320, I=288, E=6, k=1, score=synth.SCORE_SIGMOID, seed=56)
     data = synth.make_all(w)
     act = dict(kind=0, weight_on_input=True)
-    res = run_layer(w, data, block_m=64, act=act)
-    full_check(w, data, res, what="bf16/tkw1", act=act)
+    res = run_layer(w, data, block_m=bm, act=act)
+    full_check(w, data, res, what=f"bf16/tkw1/bm{bm}", act=act)
 
 
-def test_bf16_default_block_m_is_at_least_64():
-    """The layer picks 16-row blocks for small batches of quantised weights; bf16
-    weights take 64-row blocks instead."""
-    w = small(BF, T=8, H=256, I=256, E=16, k=2, seed=57)
+@pytest.mark.parametrize("H,want", [(256, 16), (3072, 64)])
+def test_bf16_default_block_m(H, want):
+    """Small batches take 16-row blocks while the activation tile fits the persistent
+    kernel (H, I <= 2944) and 64-row blocks past that."""
+    w = small(BF, T=8, H=H, I=256, E=16, k=2, seed=57)
     data = synth.make_all(w)
     res = run_layer(w, data)
-    assert res["bm"] == 64
-    full_check(w, data, res, what="bf16/default-bm")
+    assert res["bm"] == want
+    full_check(w, data, res, what=f"bf16/default-bm/H{H}")
 
 
 def test_bf16_decode_full_size():

@@ -70,6 +70,7 @@ CASES = [
     ("fp8-channel", lambda: small(FP8C, T=16, H=512, I=384, E=8, k=2, seed=25), True, True),
     ("e64-max-batch", lambda: small(W4A16, T=128, H=256, I=256, E=64, k=32, seed=26), False, False),
     ("t-max", lambda: small(W4A16, T=1024, H=256, I=128, E=8, k=4, seed=27), True, False),
+    ("bf16-weights", lambda: small((synth.W_BF16, synth.A_BF16), T=45, H=320, I=288, E=8, k=2, seed=33), False, True),
 ]
 
 
