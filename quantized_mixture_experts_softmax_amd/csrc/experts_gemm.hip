@@ -47,6 +47,9 @@ constexpr int kXcds = 8;
 #ifndef MOE_KSPLIT_NT_BF16
 #define MOE_KSPLIT_NT_BF16 8
 #endif
+#ifndef MOE_DMA_A  // 64/128-row kernel, bf16 activations: A tile global -> LDS by direct loads
+#define MOE_DMA_A 1
+#endif
 #ifndef MOE_SCALE_DWORD
 #define MOE_SCALE_DWORD 1
 #endif
@@ -92,6 +95,26 @@ __device__ __forceinline__ uint32_t ld8(const uint8_t* base, size_t off, bool ok
 __device__ __forceinline__ float ldf(const float* base, size_t off, bool ok) {
   return ld_global<float>(base, off * sizeof(float), ok);
 }
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt at their maxima, i.e.
+// not waited for).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return ((n > 63 ? 63 : n) & 0xF) | (((n > 63 ? 63 : n) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+
+// Direct global -> LDS load of 16 bytes per lane: the wave's 64 x 16 bytes land
+// contiguously at dst (wave-uniform).  Counted by vmcnt like any other load.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 16, 0, 0);
+}
+// The same with 4 bytes per lane: 256 contiguous bytes at dst.
+__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 4, 0, 0);
+}
+
 // A read-only fp32 at a wave-uniform address through the scalar data cache (a load from
 // the constant address space; the cache is invalidated at each dispatch and nothing in the
 // kernel writes the data).
@@ -183,6 +206,11 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
 
   // ---- A rows this thread stages into LDS ----
+  // kDmaA (bf16 A, one-chunk-ahead loop): direct global -> LDS loads into an unpadded tile
+  // (256 B rows); position pv of row r holds the row's 16-byte unit pv ^ (r % 16), so the
+  // 16 rows of a fragment read fall in 16 different bank groups.  The data never passes
+  // through registers, which takes it off the vector-memory return path.
+  constexpr bool kDmaA = (AF == kABf16) && (MOE_DMA_A != 0);
   const uint8_t* a_src[AIT];
   bool a_ok[AIT];
   int a_lds[AIT], a_k0[AIT];
@@ -201,10 +229,11 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         arow = b * BM + r;
       }
     }
-    a_src[it] = (const uint8_t*)p.a + (size_t)arow * a_row_bytes + pc * 16;
+    const int pu = kDmaA ? (pc ^ (r & (APC - 1))) : pc;  // the row's unit this thread moves
+    a_src[it] = (const uint8_t*)p.a + (size_t)arow * a_row_bytes + pu * 16;
     a_ok[it] = ok;
     a_lds[it] = (piece < NPIECE ? r : 0) * LROW + pc * 16;
-    a_k0[it] = pc * EPP;
+    a_k0[it] = pu * EPP;
   }
   // ---- activation scale row owned by thread tid < BM ----
   int s_row = 0;
@@ -364,7 +393,9 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       for (int st = 0; st < 4; ++st) {
         bf16x8 af[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) af[m] = *(const bf16x8*)(la + (m * 16 + li) * LROW + 64 * g + 16 * st);
+        for (int m = 0; m < MT; ++m)
+          af[m] = kDmaA ? *(const bf16x8*)(la + (m * 16 + li) * ARB + 16 * ((4 * g + st) ^ li))
+                        : *(const bf16x8*)(la + (m * 16 + li) * LROW + 64 * g + 16 * st);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           bf16x8 bfr;
@@ -454,7 +485,39 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   constexpr int kPF = (AF == kABf16) ? MOE_PF_BF16
                                      : (AF == kAMxfp4 ? MOE_PF_F4A4 : (WF == kWFp8Channel ? MOE_PF_F8C : MOE_PF_F8B));
   auto chunk_barrier = [] { lds_barrier(); };
-  if constexpr (kPF == 0) {
+  // kDmaA: chunk c's A tile straight into LDS buffer buf (each wave's 64 pieces of a round
+  // are 1 KB contiguous); rows past the batch and K past the end read the zero page
+  auto dma_a = [&](int c, int buf) {
+#pragma unroll
+    for (int it = 0; it < AIT; ++it) {
+      const bool ok = a_ok[it] && (c * 128 + a_k0[it] < K);
+      const MOE_GLOBAL uint8_t* src =
+          ok ? (const MOE_GLOBAL uint8_t*)a_src[it] + (size_t)c * ARB : (const MOE_GLOBAL uint8_t*)kZeroPage;
+      dma16((const void*)src, &lds_a[buf][(size_t)(64 * w + 256 * it) * 16]);
+    }
+  };
+  static_assert(!kDmaA || kPF == 0, "the direct-load A tile runs in the one-chunk-ahead loop");
+  if constexpr (kPF == 0 && kDmaA) {
+    // every load of a chunk (its A tile and the next chunk's weights) is waited for at the
+    // chunk's end, before the barrier that hands the tile to the other waves
+    WeightRegs<WF, NT> wr, wn;
+    dma_a(0, 0);
+    load_w(0, wr);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    chunk_barrier();
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < nch;
+      if (more) {
+        dma_a(c + 1, buf ^ 1);
+        load_w(c + 1, wn);
+      }
+      compute(buf, wr);
+      if (more) wr = wn;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      chunk_barrier();
+    }
+  } else if constexpr (kPF == 0) {
     i32x4 areg[AIT];
     float fs = 0.f;
     uint32_t qs = 0;
@@ -936,26 +999,6 @@ __host__ __device__ inline size_t tile16_lds_bytes(int afmt, int K) {
   if (afmt == kAMxfp4) sc = 16 * (size_t)nch * 4;
   if (afmt == kAFp8Token) sc = 16 * 4;
   return (tile + 192 + sc + 255) / 256 * 256;
-}
-
-// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
-// encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt at their maxima, i.e.
-// not waited for).
-__host__ __device__ constexpr int vmcnt_imm(int n) {
-  return ((n > 63 ? 63 : n) & 0xF) | (((n > 63 ? 63 : n) >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
-
-// Direct global -> LDS load of 16 bytes per lane: the wave's 64 x 16 bytes land
-// contiguously at dst (wave-uniform).  Counted by vmcnt like any other load.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 16, 0, 0);
-}
-// The same with 4 bytes per lane: 256 contiguous bytes at dst.
-__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void*)src, (lds_void*)dst, 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------
