@@ -50,6 +50,9 @@ constexpr int kXcds = 8;
 #ifndef MOE_DMA_A  // 64/128-row kernel, bf16 activations: A tile global -> LDS by direct loads
 #define MOE_DMA_A 1
 #endif
+#ifndef MOE_DMA_AQ  // the same for the quantised activation formats, one chunk ahead: measured
+#define MOE_DMA_AQ 0  // slower than their register rings (w4a4 -1%, FP8 block -4%, FP8 channel -17%)
+#endif
 #ifndef MOE_SCALE_DWORD
 #define MOE_SCALE_DWORD 1
 #endif
@@ -206,11 +209,13 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
 
   // ---- A rows this thread stages into LDS ----
-  // kDmaA (bf16 A, one-chunk-ahead loop): direct global -> LDS loads into an unpadded tile
-  // (256 B rows); position pv of row r holds the row's 16-byte unit pv ^ (r % 16), so the
-  // 16 rows of a fragment read fall in 16 different bank groups.  The data never passes
-  // through registers, which takes it off the vector-memory return path.
-  constexpr bool kDmaA = (AF == kABf16) && (MOE_DMA_A != 0);
+  // kDmaA (one-chunk-ahead loop): direct global -> LDS loads into an unpadded tile (ARB-byte
+  // rows); position pv of row r holds the row's 16-byte unit pv ^ aswz(r), so the 16 rows
+  // of a fragment read fall in 16 different bank groups.  The data never passes through
+  // registers, which takes it off the vector-memory return path.
+  constexpr bool kDmaA = (AF == kABf16) ? (MOE_DMA_A != 0) : (MOE_DMA_AQ != 0);
+  constexpr int RPB = 256 / ARB;  // tile rows per 256 bytes
+  auto aswz = [](int r) { return (r / RPB) & (APC - 1); };
   const uint8_t* a_src[AIT];
   bool a_ok[AIT];
   int a_lds[AIT], a_k0[AIT];
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         arow = b * BM + r;
       }
     }
-    const int pu = kDmaA ? (pc ^ (r & (APC - 1))) : pc;  // the row's unit this thread moves
+    const int pu = kDmaA ? (pc ^ aswz(r)) : pc;  // the row's unit this thread moves
     a_src[it] = (const uint8_t*)p.a + (size_t)arow * a_row_bytes + pu * 16;
     a_ok[it] = ok;
     a_lds[it] = (piece < NPIECE ? r : 0) * LROW + pc * 16;
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         bf16x8 af[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          af[m] = kDmaA ? *(const bf16x8*)(la + (m * 16 + li) * ARB + 16 * ((4 * g + st) ^ li))
+          af[m] = kDmaA ? *(const bf16x8*)(la + (m * 16 + li) * ARB + 16 * ((4 * g + st) ^ aswz(m * 16 + li)))
                         : *(const bf16x8*)(la + (m * 16 + li) * LROW + 64 * g + 16 * st);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -419,7 +424,8 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       // w4a4: scaled FP4 MFMA, E8M0 bytes as operand scales
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const i32x4 a4 = *(const i32x4*)(la + (m * 16 + li) * LROW + 16 * g);
+        const i32x4 a4 = kDmaA ? *(const i32x4*)(la + (m * 16 + li) * ARB + 16 * (g ^ aswz(m * 16 + li)))
+                               : *(const i32x4*)(la + (m * 16 + li) * LROW + 16 * g);
         const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
         const int sa = (int)((lds_as4[buf][m * 16 + li] >> (8 * g)) & 0xFFu);
 #pragma unroll
@@ -433,8 +439,11 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       // FP8 e4m3 x e4m3 at unit operand scale
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const i32x4 lo = *(const i32x4*)(la + (m * 16 + li) * LROW + 32 * g);
-        const i32x4 hi = *(const i32x4*)(la + (m * 16 + li) * LROW + 32 * g + 16);
+        const int R = m * 16 + li;
+        const i32x4 lo = kDmaA ? *(const i32x4*)(la + R * ARB + 16 * ((2 * g) ^ aswz(R)))
+                               : *(const i32x4*)(la + R * LROW + 32 * g);
+        const i32x4 hi = kDmaA ? *(const i32x4*)(la + R * ARB + 16 * ((2 * g + 1) ^ aswz(R)))
+                               : *(const i32x4*)(la + R * LROW + 32 * g + 16);
         const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         float asr[4];
         if constexpr (WF == kWFp8Block) {
@@ -496,13 +505,23 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       dma16((const void*)src, &lds_a[buf][(size_t)(64 * w + 256 * it) * 16]);
     }
   };
-  static_assert(!kDmaA || kPF == 0, "the direct-load A tile runs in the one-chunk-ahead loop");
-  if constexpr (kPF == 0 && kDmaA) {
-    // every load of a chunk (its A tile and the next chunk's weights) is waited for at the
-    // chunk's end, before the barrier that hands the tile to the other waves
+  auto store_as = [&](int buf, float fs, uint32_t qs) {
+    if (tid < BM) {
+      if constexpr (AF == kAFp8G128) lds_as[buf][tid] = fs;
+      if constexpr (AF == kAMxfp4) lds_as4[buf][tid] = qs;
+    }
+  };
+  if constexpr (kDmaA) {
+    // one chunk ahead: every load of a chunk (its A tile, the next chunk's activation scales
+    // and weights) is waited for at the chunk's end, before the barrier that hands the
+    // tile to the other waves
     WeightRegs<WF, NT> wr, wn;
+    float fs = 0.f;
+    uint32_t qs = 0;
     dma_a(0, 0);
+    load_as(0, fs, qs);
     load_w(0, wr);
+    store_as(0, fs, qs);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     chunk_barrier();
     for (int c = 0; c < nch; ++c) {
@@ -510,10 +529,14 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       const bool more = c + 1 < nch;
       if (more) {
         dma_a(c + 1, buf ^ 1);
+        load_as(c + 1, fs, qs);
         load_w(c + 1, wn);
       }
       compute(buf, wr);
-      if (more) wr = wn;
+      if (more) {
+        store_as(buf ^ 1, fs, qs);
+        wr = wn;
+      }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       chunk_barrier();
     }
