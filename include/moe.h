@@ -232,7 +232,8 @@ moe_status moe_route_align(const float* router_logits, int T, int E, int topk, m
  *   x       [rows, cols] bf16;  codes / scales: layouts of moe_afmt above.
  * MOE_A_FP8_TENSOR runs four launches (the scale slot holds the amax until the last one)
  * and needs rows * cols < 2^31.
- * Limits: cols % 32 == 0, cols <= 65536, rows >= 0.  fmt == MOE_A_BF16 is MOE_EINVAL.
+ * Limits: cols % 32 == 0, cols <= 65536, rows >= 0.  x and codes 16-byte aligned, scales
+ * 4-byte aligned.  fmt == MOE_A_BF16 is MOE_EINVAL.
  * ---------------------------------------------------------------------------------- */
 moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt,
                          uint8_t* codes, void* scales, hipStream_t stream);

@@ -289,7 +289,8 @@ moe_status moe_quant_act(const uint16_t* x, int rows, int cols, moe_afmt fmt, ui
   if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_EINVAL, "moe_quant_act: NULL pointer");
   if (fmt == MOE_A_FP8_TENSOR && (long long)rows * cols >= 0x7FFFFFFFLL)
     return fail(MOE_EINVAL, "moe_quant_act: per-tensor quantisation needs rows * cols < 2^31");
-  if (!aligned(x, 4) || !aligned(codes, 2) || !aligned(scales, 4)) return fail(MOE_EINVAL, "moe_quant_act: misaligned pointer");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(MOE_EINVAL, "moe_quant_act: x and codes must be 16-byte aligned, scales 4-byte aligned");
   return hip_status(moe::launch_quant_act(x, rows, cols, (int)fmt, nullptr, codes, scales, stream), "moe_quant_act launch");
 }
 

@@ -15,27 +15,54 @@
 
 namespace moe {
 
-// FP8, 128-column groups: one wave per (row, group), two columns per lane.
+// Eight bf16 values (16 bytes, 16-byte aligned) as fp32; zeros when !ok.
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, bool ok, float (&f)[8]) {
+  const uint4 v = ok ? *(const uint4*)p : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+__device__ __forceinline__ float amax8(const float (&f)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  return m;
+}
+// e4m3 codes of f[i] / s, packed little-endian into 8 bytes
+__device__ __forceinline__ uint2 e4m3_pack8(const float (&f)[8], float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= e4m3_encode(f[i] / s) << (8 * i);
+    hi |= e4m3_encode(f[4 + i] / s) << (8 * i);
+  }
+  return make_uint2(lo, hi);
+}
+
+// FP8, 128-column groups: 16 lanes per (row, group), eight columns (16 bytes) per lane.
+// Every lane takes part in the group reduction (no early return before the shuffles).
 __global__ __launch_bounds__(256) void quant_fp8_g128_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                              const int32_t* __restrict__ rows_dev,
                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int ng = (cols + 127) / 128;
-  const long gid = (long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (gid >= (long)rows * ng) return;
-  const int r = (int)(gid / ng), g = (int)(gid % ng);
-  if (rows_dev && r >= rows_dev[0]) return;
-  const int lane = lane_id();
-  const int c = g * 128 + 2 * lane;
-  const bool ok = c < cols;
-  uint32_t pair = ok ? *(const uint32_t*)(x + (size_t)r * cols + c) : 0u;
-  const float v0 = bf16_to_f32(pair & 0xFFFFu), v1 = bf16_to_f32(pair >> 16);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  if (ok) {
-    const uint32_t q = e4m3_encode(v0 / s) | (e4m3_encode(v1 / s) << 8);
-    *(uint16_t*)(codes + (size_t)r * cols + c) = (uint16_t)q;
-  }
-  if (lane == 0) scales[(size_t)r * ng + g] = s;
+  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = (int)(threadIdx.x & 15);
+  const bool in = gid < (long)rows * ng;
+  const int r = in ? (int)(gid / ng) : 0, g = in ? (int)(gid % ng) : 0;
+  const bool live = in && !(rows_dev && r >= rows_dev[0]);
+  const int c = g * 128 + 8 * sub;
+  const bool ok = live && c < cols;  // cols % 32 == 0: eight columns are all in or all out
+  float f[8];
+  load8_bf16(x + (size_t)r * cols + c, ok, f);
+  float m = amax8(f);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  if (ok) *(uint2*)(codes + (size_t)r * cols + c) = e4m3_pack8(f, s);
+  if (live && sub == 0) scales[(size_t)r * ng + g] = s;
 }
 
 // FP8, one scale per row: one 256-thread workgroup per row.
@@ -47,43 +74,49 @@ __global__ __launch_bounds__(256) void quant_fp8_token_kernel(const uint16_t* __
   __shared__ float red[4];
   const uint16_t* xr = x + (size_t)r * cols;
   float m = 0.0f;
-  for (int c = 2 * (int)threadIdx.x; c < cols; c += 512) {
-    const uint32_t pair = *(const uint32_t*)(xr + c);
-    m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(pair & 0xFFFFu)), fabsf(bf16_to_f32(pair >> 16))));
+  for (int c = 8 * (int)threadIdx.x; c < cols; c += 2048) {  // cols % 32 == 0
+    float f[8];
+    load8_bf16(xr + c, true, f);
+    m = fmaxf(m, amax8(f));
   }
   m = wave_max(m);
   if (lane_id() == 0) red[threadIdx.x / kWave] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  for (int c = 2 * (int)threadIdx.x; c < cols; c += 512) {
-    const uint32_t pair = *(const uint32_t*)(xr + c);
-    const uint32_t q = e4m3_encode(bf16_to_f32(pair & 0xFFFFu) / s) | (e4m3_encode(bf16_to_f32(pair >> 16) / s) << 8);
-    *(uint16_t*)(codes + (size_t)r * cols + c) = (uint16_t)q;
+  for (int c = 8 * (int)threadIdx.x; c < cols; c += 2048) {
+    float f[8];
+    load8_bf16(xr + c, true, f);
+    *(uint2*)(codes + (size_t)r * cols + c) = e4m3_pack8(f, s);
   }
   if (threadIdx.x == 0) scales[r] = s;
 }
 
-// MXFP4, 32-column groups: 16 lanes per group, two columns (one output byte) per lane.
+// MXFP4, 32-column groups: 4 lanes per group, eight columns (16 bytes in, 4 code bytes
+// out) per lane.
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                           const int32_t* __restrict__ rows_dev,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const long pairs_per_row = cols / 2;
-  const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;  // pair index
-  const bool in = p < (long)rows * pairs_per_row;
-  const int r = in ? (int)(p / pairs_per_row) : 0;
-  const int c = in ? (int)(p % pairs_per_row) * 2 : 0;
+  const long per_row = cols / 8;
+  const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;  // index of 8 consecutive columns
+  const bool in = q < (long)rows * per_row;
+  const int r = in ? (int)(q / per_row) : 0;
+  const int c = in ? (int)(q % per_row) * 8 : 0;
   const bool live = in && !(rows_dev && r >= rows_dev[0]);
-  const uint32_t pair = live ? *(const uint32_t*)(x + (size_t)r * cols + c) : 0u;
-  const float v0 = bf16_to_f32(pair & 0xFFFFu), v1 = bf16_to_f32(pair >> 16);
-  float m = fmaxf(fabsf(v0), fabsf(v1));
-  // groups are 16 consecutive lanes (cols % 32 == 0 keeps groups inside one row)
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  float f[8];
+  load8_bf16(x + (size_t)r * cols + c, live, f);
+  float m = amax8(f);
+  // groups are 4 consecutive lanes (cols % 32 == 0 keeps groups inside one row)
+  m = fmaxf(m, __shfl_xor(m, 2, kWave));
+  m = fmaxf(m, __shfl_xor(m, 1, kWave));
   const int es = mx_shared_exp(m);
   const float inv = exp2i(-es);
   if (live) {
-    codes[(size_t)r * (cols / 2) + c / 2] = (uint8_t)(e2m1_encode(v0 * inv) | (e2m1_encode(v1 * inv) << 4));
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      packed |= (e2m1_encode(f[2 * i] * inv) | (e2m1_encode(f[2 * i + 1] * inv) << 4)) << (8 * i);
+    *(uint32_t*)(codes + (size_t)r * (cols / 2) + c / 2) = packed;
     if ((c & 31) == 0) scales[(size_t)r * (cols / 32) + c / 32] = (uint8_t)(es + 127);
   }
 }
@@ -145,15 +178,15 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
     return hipGetLastError();
   }
   if (fmt == kAFp8G128) {
-    const long groups = (long)rows * ((cols + 127) / 128);
-    quant_fp8_g128_kernel<<<(unsigned)((groups + 3) / 4), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
-                                                                              (float*)scales);
+    const long groups = (long)rows * ((cols + 127) / 128);  // 16 per 256-thread workgroup
+    quant_fp8_g128_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
+                                                                                (float*)scales);
   } else if (fmt == kAFp8Token) {
     quant_fp8_token_kernel<<<(unsigned)rows, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, (float*)scales);
   } else {
-    const long pairs = (long)rows * (cols / 2);
-    quant_mxfp4_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
-                                                                             (uint8_t*)scales);
+    const long octs = (long)rows * (cols / 8);
+    quant_mxfp4_kernel<<<(unsigned)((octs + 255) / 256), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
+                                                                            (uint8_t*)scales);
   }
   return hipGetLastError();
 }

@@ -106,6 +106,10 @@ def test_quant_rejects(lib):
     assert lib.moe_quant_act(P(FAKE), 4, 100, B.A_FP8_G128, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
     assert lib.moe_quant_act(P(FAKE), 4, 128, B.A_BF16, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
     assert lib.moe_quant_act(P(FAKE + 1), 4, 128, B.A_FP8_G128, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    # the quantisers move 16 bytes per lane: x and codes 16-byte aligned
+    assert lib.moe_quant_act(P(FAKE + 8), 4, 128, B.A_MXFP4_G32, P(FAKE), P(FAKE), None) == B.MOE_EINVAL
+    assert lib.moe_quant_act(P(FAKE), 4, 128, B.A_FP8_TOKEN, P(FAKE + 8), P(FAKE), None) == B.MOE_EINVAL
+    assert "16-byte" in B.moe_last_error()
 
 
 def _args(**kw):
