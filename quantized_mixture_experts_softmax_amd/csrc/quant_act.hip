@@ -132,11 +132,12 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t* __rest
                                                           uint32_t* __restrict__ acc) {
   __shared__ float red[4];
   const int n_rows = rows_dev ? min(rows, rows_dev[0]) : rows;
-  const long pairs = (long)n_rows * (cols / 2);
+  const long octs = (long)n_rows * (cols / 8);  // 8 elements (16 bytes) per step
   float m = 0.0f;
-  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < pairs; q += (long)gridDim.x * blockDim.x) {
-    const uint32_t pair = *(const uint32_t*)(x + 2 * q);
-    m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(pair & 0xFFFFu)), fabsf(bf16_to_f32(pair >> 16))));
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < octs; q += (long)gridDim.x * blockDim.x) {
+    float f[8];
+    load8_bf16(x + 8 * q, true, f);
+    m = fmaxf(m, amax8(f));
   }
   m = wave_max(m);
   if (lane_id() == 0) red[threadIdx.x / kWave] = m;
@@ -151,11 +152,11 @@ __global__ __launch_bounds__(256) void quant_fp8_tensor_kernel(const uint16_t* _
   const float amax = __uint_as_float(acc[0]);
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   const int n_rows = rows_dev ? min(rows, rows_dev[0]) : rows;
-  const long pairs = (long)n_rows * (cols / 2);
-  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < pairs; q += (long)gridDim.x * blockDim.x) {
-    const uint32_t pair = *(const uint32_t*)(x + 2 * q);
-    const uint32_t c = e4m3_encode(bf16_to_f32(pair & 0xFFFFu) / s) | (e4m3_encode(bf16_to_f32(pair >> 16) / s) << 8);
-    *(uint16_t*)(codes + 2 * q) = (uint16_t)c;
+  const long octs = (long)n_rows * (cols / 8);
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < octs; q += (long)gridDim.x * blockDim.x) {
+    float f[8];
+    load8_bf16(x + 8 * q, true, f);
+    *(uint2*)(codes + 8 * q) = e4m3_pack8(f, s);
   }
 }
 
@@ -168,8 +169,8 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
                             uint8_t* codes, void* scales, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (fmt == kAFp8Tensor) {
-    const long pairs = (long)rows * (cols / 2);
-    const unsigned g = (unsigned)std::min<long>((pairs + 255) / 256, 4096);
+    const long octs = (long)rows * (cols / 8);
+    const unsigned g = (unsigned)std::min<long>((octs + 255) / 256, 4096);
     uint32_t* acc = (uint32_t*)scales;
     tensor_amax_zero_kernel<<<1, 1, 0, stream>>>(acc);
     tensor_amax_kernel<<<g, 256, 0, stream>>>(x, rows, cols, rows_dev, acc);
