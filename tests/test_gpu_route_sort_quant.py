@@ -149,7 +149,11 @@ QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8
                ("fp8-token", B.A_FP8_TOKEN, 40, 4096), ("fp8-token-wide", B.A_FP8_TOKEN, 3, 14336),
                ("mxfp4", B.A_MXFP4_G32, 40, 2880), ("mxfp4-small", B.A_MXFP4_G32, 1, 32),
                ("fp8-tensor", B.A_FP8_TENSOR, 40, 4096), ("fp8-tensor-big", B.A_FP8_TENSOR, 4096, 7168),
-               ("fp8-tensor-one", B.A_FP8_TENSOR, 1, 32)]
+               ("fp8-tensor-one", B.A_FP8_TENSOR, 1, 32),
+               # eight columns per lane: a row narrower than one pass of the workgroup, an
+               # odd number of 32-groups, and a last 128-group half full
+               ("fp8-token-narrow", B.A_FP8_TOKEN, 5, 96), ("mxfp4-odd-groups", B.A_MXFP4_G32, 9, 96),
+               ("fp8-g128-half-group", B.A_FP8_G128, 7, 2880), ("fp8-tensor-narrow", B.A_FP8_TENSOR, 3, 96)]
 
 
 @pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
