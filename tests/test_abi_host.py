@@ -232,3 +232,11 @@ def test_bf16_layer_rejects_on_host():
     with pytest.raises(ValueError, match="block_m"):
         B.MoELayer(torch.zeros((2, 64, 3072), dtype=torch.bfloat16), None,
                    torch.zeros((2, 3072, 32), dtype=torch.bfloat16), None, block_m=16, **big)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """Without the built HIP library the binding raises; it has no CPU fallback."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    with pytest.raises(RuntimeError, match="libmoe.so not found"):
+        B.moe_pick_block_m(64, 4, 32)
