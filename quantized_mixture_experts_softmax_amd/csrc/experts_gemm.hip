@@ -36,6 +36,7 @@
 #include "sort_device.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace moe {
 
@@ -1524,16 +1525,18 @@ constexpr size_t kPersistLdsFusedMax = 160 * 1024;
 #define MOE_PERSIST_DEPTH_F8B 2
 #endif
 
+// Per-device caches below: atomics, since host threads may launch on several devices at once
+// (two threads filling one entry store the same value).
 static int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // LDS bytes of the persistent kernel: activation tile + one partial-sum slot per wave.
@@ -1544,16 +1547,16 @@ static size_t persist_lds_bytes(int afmt, int K, int waves) {
 // Dynamic LDS a persistent workgroup may take on the current device: kPersistLdsFusedMax,
 // or less where the device's per-workgroup limit is lower.
 static size_t persist_lds_limit() {
-  static int lim[64] = {0};
+  static std::atomic<int> lim[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
-  if (lim[dev] == 0) {
-    int n = 0;
+  int n = lim[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0)
       n = 64 * 1024;
-    lim[dev] = n;
+    lim[dev].store(n, std::memory_order_relaxed);
   }
-  return std::min((size_t)lim[dev], kPersistLdsFusedMax);
+  return std::min((size_t)n, kPersistLdsFusedMax);
 }
 
 // Bytes of the persistent kernel's bias slice: one phase covers at most the U units of a
@@ -1600,12 +1603,15 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
                                                     : (WF == kWFp8Block ? MOE_PERSIST_DEPTH_F8B : MOE_PERSIST_DEPTH_F8));
   if (p.num_blocks == 0) return hipSuccess;
   auto kern = moe_gemm_persist_kernel<STAGE, WF, AF, D, WAVES, WL, EPI, RS>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic-LDS limit is raised once per kernel and device (setting it twice is harmless)
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  const bool cached = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  if (!cached || !attr_set[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)persist_lds_limit());
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (cached) attr_set[dev].store(true, std::memory_order_release);
   }
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 64 * WAVES, lds);
