@@ -103,14 +103,25 @@ def mfma_dtype(w):
     return "fp8"
 
 
+# Sources compiled into the grouped-GEMM kernels (the route + sort fused into stage 1
+# comes from sort_device.h): a counter summary is current only for these bytes.
+GEMM_SOURCES = ("experts_gemm.hip", "moe_device.h", "moe_internal.h", "sort_device.h")
+
+
+def gemm_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "quantized_mixture_experts_softmax_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profiles(workload_name: str):
     """HBM bytes per stage-1 launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (else None)."""
+    was taken on the current kernel sources (else None)."""
     path = os.path.join(PROFILES, f"gemm1_{workload_name}_pmc.txt")
-    src = os.path.join(ROOT, "quantized_mixture_experts_softmax_amd", "csrc", "experts_gemm.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = gemm_source_sha()
     vals = {}
     for line in open(path):
         if "=" in line and line.strip().startswith("TRAFFIC_"):
