@@ -196,8 +196,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU (expert/tensor parallel) path is "
-              "described in DESIGN.md and not implemented. Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU; the sharded multi-GPU (expert / tensor parallel) path is not "
+              "implemented. Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
