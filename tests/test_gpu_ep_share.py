@@ -32,12 +32,13 @@ def run_share(w, data, ids_dev, wts_dev, mine, bm, tiled, n_valid=None):
     E_loc = len(mine)
     emap = np.full(w.E_total, -1, np.int32)
     emap[mine] = np.arange(E_loc, dtype=np.int32)
-    pick = lambda a: np.ascontiguousarray(a[mine])
+    pick = lambda a: None if a is None else np.ascontiguousarray(a[mine])
     wl = {k: pick(data[k]) for k in ("w1", "w1_scale", "w2", "w2_scale")}
+    dev = lambda a: None if a is None else (bf16_dev(a) if a.dtype == np.uint16 else to_dev(a))
     nv = None if n_valid is None else to_dev(np.array([n_valid], np.int32))
     loc = B.moe_map_experts(ids_dev, to_dev(emap), w.E_total, nv)
     srt = B.moe_align_sort(loc, E_loc, bm)
-    w1, w1s, w2, w2s = (to_dev(wl[k]) for k in ("w1", "w1_scale", "w2", "w2_scale"))
+    w1, w1s, w2, w2s = (dev(wl[k]) for k in ("w1", "w1_scale", "w2", "w2_scale"))
     layout = B.LAYOUT_CANONICAL
     if tiled:
         w1, w2 = B.moe_tile_weights(w1, w1s, w.wfmt, w.H), B.moe_tile_weights(w2, w2s, w.wfmt, w.I)
@@ -60,10 +61,13 @@ def run_share(w, data, ids_dev, wts_dev, mine, bm, tiled, n_valid=None):
     return res, Lo
 
 
-@pytest.mark.parametrize("name,bm,tiled", [("decode", 16, True), ("tiny", 64, False), ("fp8c", 32, True)])
+@pytest.mark.parametrize("name,bm,tiled", [("decode", 16, True), ("tiny", 64, False), ("fp8c", 32, True),
+                                           ("bf16", 16, False), ("bf16", 64, False)])
 def test_ep_shares(name, bm, tiled):
     if name == "fp8c":
         w = synth.Workload("fp8c", 16, 256, 512, 8, 2, synth.W_FP8_CHANNEL, synth.A_FP8_TOKEN, seed=77)
+    elif name == "bf16":
+        w = synth.Workload("bf16", 48, 320, 288, 16, 3, synth.W_BF16, synth.A_BF16, seed=78)
     else:
         w = synth.WORKLOADS[name]
     data = synth.make_all(w)
