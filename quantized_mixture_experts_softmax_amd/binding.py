@@ -404,7 +404,14 @@ class MoELayer:
     """Device-resident weights of one quantised MoE expert layer and the full hot
     path: route + align-sort, optional a1 quantisation, experts forward (one
     moe_layer_forward call, or moe_route_align + moe_experts_forward with
-    fuse_route=False).  Buffers are allocated on first use and reused."""
+    fuse_route=False).
+
+    Every call returns a new output tensor.  The routing tables, a1 codes and the
+    workspace are allocated on first use for a token count and reused by later calls with
+    that count, so two calls on different streams must not overlap (the second would
+    overwrite the first's intermediates); a call on a stream other than the current one
+    records that stream on the reused buffers, so the caching allocator does not hand
+    their memory out while its kernels may still run."""
 
     def __init__(self, w1, w1_scale, w2, w2_scale, *, H: int, I: int, E: int, topk: int, wfmt: int, afmt: int,
                  score: str = "softmax", n_shared: int = 0, shared_weight: float = 1.0, block_m: int | None = None,
@@ -465,7 +472,6 @@ class MoELayer:
                     sorted_slots=torch.empty(cap, dtype=torch.int32, device=dev),
                     block_expert=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
                     num_padded=torch.empty(1, dtype=torch.int32, device=dev)),
-                out=torch.empty((T, self.H), dtype=torch.bfloat16, device=dev),
                 workspace=None, a1=None,
             )
             if self.afmt != A_BF16:
@@ -474,9 +480,28 @@ class MoELayer:
             self._bufs = {key: b}
         return self._bufs[key]
 
+    def _record(self, b: dict, stream, dev) -> None:
+        """Marks every reused buffer as in use on `stream` when it is not the current one."""
+        if stream is None or stream == torch.cuda.current_stream(dev):
+            return
+        ts = [b["ids"], b["ids_global"], b["w"], *b["sort"].values(), *(b["a1"] or ())]
+        if b["workspace"] is not None:
+            ts.append(b["workspace"])
+        for t in ts:
+            t.record_stream(stream)
+
     def __call__(self, x: torch.Tensor, router_logits: torch.Tensor, stream=None) -> torch.Tensor:
         T = x.shape[0]
         b = self._buffers(T, x.device)
+        out = torch.empty((T, self.H), dtype=torch.bfloat16, device=x.device)
+        if stream is not None and stream != torch.cuda.current_stream(x.device):
+            out.record_stream(stream)
+        try:
+            return self._forward(x, router_logits, b, out, stream)
+        finally:
+            self._record(b, stream, x.device)
+
+    def _forward(self, x, router_logits, b, out, stream):
         if self.fuse_route and self.expert_map is None and self.grouped is None:
             a1c = a1s = None
             if self.afmt != A_BF16:
@@ -484,7 +509,7 @@ class MoELayer:
             out, b["workspace"] = moe_layer_forward(
                 x, router_logits, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"],
                 self.wfmt, self.afmt, b["bm"], self.E_local, self.I, self.score, True, self.n_shared,
-                self.shared_weight, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
+                self.shared_weight, out, b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
             return out
         if self.expert_map is not None:
             moe_route_topk(router_logits, self.topk, self.score, True, self.n_shared, self.shared_weight,
@@ -505,5 +530,5 @@ class MoELayer:
             a1c, a1s = moe_quant_act(x, self.afmt, b["a1"][0], b["a1"][1], stream)
         out, b["workspace"] = moe_experts_forward(
             x, self.w1, self.w1_scale, self.w2, self.w2_scale, b["ids"], b["w"], b["sort"], self.wfmt, self.afmt,
-            b["bm"], self.E_local, self.I, b["out"], b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
+            b["bm"], self.E_local, self.I, out, b["workspace"], a1c, a1s, stream, self.weight_layout, self.act)
         return out

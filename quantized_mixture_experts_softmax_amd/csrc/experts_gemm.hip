@@ -613,6 +613,13 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
     float bsv[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) bsv[t] = (EPI && p.bias && col_ok[t]) ? bias_of(p, e, wrow[t]) : 0.0f;
+    // pad rows: h is written as 0 (without a bias their projections are 0 and so is h; with
+    // one, act(bias) must not reach the a2 quantiser, whose per-tensor scale covers all rows)
+    bool padr[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) padr[m][rr] = EPI && p.bias && p.sorted_slots[b * BM + m * 16 + 4 * g + rr] >= TK;
     if ((EPI && p.interleaved)) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -627,7 +634,8 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
             if (EPI && p.weight_on_input) v *= fc1_weight(p, p.sorted_slots[b * BM + row]);
             v += bsv[t];
             const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
-            if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
+            if (!(li & 1))
+              p.h[(size_t)(b * BM + row) * p.N + col[t]] = padr[m][rr] ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
           }
         }
     } else {
@@ -653,7 +661,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
             }
             gv += bsv[t];
             uv += bsv[tu];
-            p.h[(size_t)(b * BM + row) * p.N + col[t]] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+            p.h[(size_t)(b * BM + row) * p.N + col[t]] = padr[m][rr] ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
           }
         }
     }
@@ -923,7 +931,8 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                 if (EPI && p.weight_on_input) v *= fc1_weight(p, p.sorted_slots[b * BM + row]);
                 v += bs;
                 const float up = __shfl_xor(v, 1, kWave);
-                if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
+                const bool pad = EPI && p.bias && !o_ok[m][rr];  // pad rows: h = 0
+                if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = pad ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
               }
           }
         } else {
@@ -953,7 +962,8 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
                 }
                 gv += bg;
                 uv += bu;
-                p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+                const bool pad = EPI && p.bias && !o_ok[m][rr];  // pad rows: h = 0
+                p.h[(size_t)(b * BM + row) * p.N + col] = pad ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
               }
           }
         }
@@ -1347,7 +1357,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               if (EPI && p.weight_on_input) v *= lds_fw[row];
               if (EPI && p.bias) v += __uint_as_float((uint32_t)lds_bias[u * 32 + t * 16 + li] << 16);
               const float up = __shfl_xor(v, 1, kWave);  // odd lane: the up row of the same column
-              if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
+              const bool pad = EPI && p.bias && lds_row[row] < 0;  // pad rows: h = 0
+              if (!(li & 1)) p.h[(size_t)(b * BM + row) * p.N + col] = pad ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, v, up));
             }
           }
         } else {
@@ -1370,7 +1381,8 @@ __global__ __launch_bounds__(64 * WAVES) void moe_gemm_persist_kernel(const Gemm
               gv += __uint_as_float((uint32_t)lds_bias[u * 32 + li] << 16);
               uv += __uint_as_float((uint32_t)lds_bias[u * 32 + 16 + li] << 16);
             }
-            p.h[(size_t)(b * BM + row) * p.N + col] = (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
+            const bool pad = EPI && p.bias && lds_row[row] < 0;  // pad rows: h = 0
+            p.h[(size_t)(b * BM + row) * p.N + col] = pad ? 0 : (uint16_t)f32_to_bf16(glu<EPI>(p, gv, uv));
           }
         }
       } else {

@@ -4,8 +4,13 @@ This module only draws random numbers in the shapes and dtypes of the workloads;
 it holds none of the layer's arithmetic (no routing, sorting, quantisation rule or
 GEMM).  The same bytes feed the HIP path and the CPU oracle.  bf16 activations
 come from fp32 normal draws through torch's bfloat16 cast (a library conversion,
-not the layer's arithmetic).  Weight codes are uniform random bytes: two uniform
-e2m1 nibbles per MXFP4 byte; FP8 bytes with the exponent field held in [4, 7].
+not the layer's arithmetic).  MXFP4 weight codes are uniform random bytes (two
+uniform e2m1 nibbles per byte).  FP8 weights are prepared the way a checkpoint's
+would be: fp32 draws from N(0, 1/K), one fp32 scale per 128x128 block, output row or
+expert equal to that block's max |w| / 448, and codes from torch's float8_e4m3fn
+cast of w / scale (a library conversion), so every e4m3 code -- zero, subnormal,
++-448 -- occurs.  fp8_weights="uniform" keeps the older draw (uniform bytes with the
+exponent field held in [4, 7]).
 
 Each tensor has its own child generator of numpy's PCG64 (SeedSequence(seed)
 spawned six ways: x, logits, w1, w1 scales, w2, w2 scales; weight codes spawn one
@@ -55,6 +60,7 @@ class Workload:
     zipf_exponent: float = 1.1
     seed: int = 1000
     T_sweep: tuple = field(default_factory=tuple)
+    fp8_weights: str = "gauss"      # "gauss": N(0, 1/K) quantised per scale block; "uniform": uniform codes
 
     @property
     def E_total(self) -> int:
@@ -182,6 +188,8 @@ def _weight(w: Workload, N: int, K: int, seq_codes, rng_scales):
             list(ex.map(fill_b, range(E)))
         return out, None
     fp8 = w.wfmt != W_MXFP4
+    if fp8 and w.fp8_weights == "gauss":
+        return _fp8_gauss_weight(w, N, K, seq_codes)
     kb = K if fp8 else K // 2
     codes = np.empty((E, N, kb), np.uint8)
     seqs = seq_codes.spawn(E)
@@ -201,6 +209,55 @@ def _weight(w: Workload, N: int, K: int, seq_codes, rng_scales):
         scales = (rng_scales.uniform(0.75, 1.25, (E,)) * base).astype(np.float32)
     else:
         scales = (rng_scales.uniform(0.75, 1.25, (E, N)) * base).astype(np.float32)
+    return codes, scales
+
+
+def _fp8_gauss_weight(w: Workload, N: int, K: int, seq_codes):
+    """FP8 weights [E, N, K] prepared like a checkpoint's: per expert, fp32 draws from
+    N(0, 1/K); per scale block (128x128 block, output row, or the whole expert) the scale is
+    that block's max |w| / 448 (1 for an all-zero block), and the codes are torch's
+    float8_e4m3fn cast of w / scale clipped to +-448.  One child generator per expert."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    E = w.E_total
+    codes = np.empty((E, N, K), np.uint8)
+    if w.wfmt == W_FP8_BLOCK128:
+        scales = np.empty((E, (N + 127) // 128, (K + 127) // 128), np.float32)
+    elif w.wfmt == W_FP8_TENSOR:
+        scales = np.empty((E,), np.float32)
+    else:
+        scales = np.empty((E, N), np.float32)
+    seqs = seq_codes.spawn(E)
+    inv_sqrt_k = np.float32(1.0 / math.sqrt(K))
+
+    def fill(e):
+        v = np.random.default_rng(seqs[e]).standard_normal((N, K), dtype=np.float32)
+        v *= inv_sqrt_k
+        a = np.abs(v)
+        if w.wfmt == W_FP8_BLOCK128:
+            nb, kb = (N + 127) // 128, (K + 127) // 128
+            pad = np.zeros((nb * 128, kb * 128), np.float32)
+            pad[:N, :K] = a
+            amax = pad.reshape(nb, 128, kb, 128).max(axis=(1, 3))
+            s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+            full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)[:N, :K]
+        elif w.wfmt == W_FP8_TENSOR:
+            amax = a.max()
+            s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+            full = s
+        else:
+            amax = a.max(axis=1)
+            s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+            full = s[:, None]
+        del a
+        q = np.clip(v / full, -448.0, 448.0).astype(np.float32)
+        codes[e] = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        scales[e] = s
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(E)))
     return codes, scales
 
 

@@ -129,7 +129,7 @@ def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dic
                sort={k: v.cpu().numpy() for k, v in b["sort"].items()}, layer=layer, bufs=b)
     if b["workspace"] is not None:
         args = B.forward_args(x, layer.w1, layer.w1_scale, layer.w2, layer.w2_scale, b["ids"], b["w"], b["sort"],
-                              w.wfmt, w.afmt, b["bm"], w.E_total, w.I, b["out"], b["workspace"],
+                              w.wfmt, w.afmt, b["bm"], w.E_total, w.I, out, b["workspace"],
                               *(b["a1"] if b["a1"] else (None, None)), weight_layout=layer.weight_layout)
         L = B.moe_workspace_layout(args)
         ws = b["workspace"]
@@ -143,6 +143,34 @@ def run_layer(w: synth.Workload, data: dict, block_m: int | None = None, wd: dic
         res["cap"] = cap
         res["ybuf_dev"] = ws[L["ybuf_off"]:L["ybuf_off"] + L["ybuf_bytes"]].view(torch.float32).view(-1, w.H)
     return res
+
+
+def targeted_tokens(res: dict, T: int, K: int, n_min: int = 16, seed: int = 0) -> np.ndarray:
+    """Tokens for a sampled full-size parity check, chosen from the routing of the run:
+    for every expert with slots, the token of its last sorted row (the expert's last,
+    usually partial, row block); the first and last tokens of the hottest expert; every
+    token of the (up to) four coldest experts; then random tokens up to n_min (at least
+    as many tokens as the oracle's threads, which parallelise over tokens)."""
+    ss = res["sort"]["sorted_slots"]
+    counts = res["sort"]["expert_counts"]
+    offs = res["sort"]["expert_offsets"]
+    pick = set()
+    hit = np.flatnonzero(counts > 0)
+    for e in hit:
+        pick.add(int(ss[offs[e] + counts[e] - 1]) // K)
+    if len(hit):
+        hot = hit[np.argmax(counts[hit])]
+        pick.add(int(ss[offs[hot]]) // K)
+        pick.add(int(ss[offs[hot] + counts[hot] - 1]) // K)
+        for e in hit[np.argsort(counts[hit], kind="stable")][:4]:
+            for r in range(offs[e], offs[e] + min(int(counts[e]), 8)):
+                pick.add(int(ss[r]) // K)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(pick, np.int64, len(pick)))
+    extra = max(0, min(n_min - len(pick), len(rest)))
+    if extra:
+        pick.update(int(t) for t in rng.choice(rest, extra, replace=False))
+    return np.array(sorted(pick), np.int32)
 
 
 def h_by_slot(res: dict, T: int, K: int, I: int) -> np.ndarray:

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from gpu_common import B, run_layer, say, synth
-from test_gpu_forward import _sample, full_check, small
+from test_gpu_forward import full_check, small
 
 pytestmark = pytest.mark.gpu
 
@@ -92,4 +92,4 @@ def test_bf16_decode_full_size():
     say(f"full-size {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.topk}")
     data = synth.make_all(w)
     res = run_layer(w, data)
-    full_check(w, data, res, tokens=_sample(w.T, 64, 9), what=w.name)
+    full_check(w, data, res, what=w.name)

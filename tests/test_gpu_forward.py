@@ -6,21 +6,29 @@ Output bound: max|gpu - oracle| <= 2e-2 * rms(oracle) and per-token relative L2 
 from the per-slot fp32 rows in the workspace); the bf16 output is separately checked
 to be that result rounded to nearest even, bit for bit.  The bound is not applied to
 the bf16 values themselves because half a bf16 ulp of the largest outputs (up to ~9x
-rms on these workloads) already exceeds 2e-2 * rms.  Stage-1 h is checked element-wise to one bf16 ulp: both
-sides round an accumulated value to bf16 and the GPU's fp32 MFMA sum runs in another
-order than the oracle's fp64 sum.  For quantised activations that one-ulp freedom can
-move an h value across an a2 rounding boundary, and a single FP4 code step is a large
-change, so those paths are checked in stages: the GPU's a2 codes bit-exactly against
-the oracle quantiser applied to the GPU's own h, and the output bound against the
-oracle's stage 2 fed the GPU's h; the end-to-end result is reported with the count of
-differing a2 codes, which must stay below 0.2%, and a per-row L2 bound.
+rms on these workloads) already exceeds 2e-2 * rms.  Stage-1 h is checked element-wise
+to one bf16 ulp: both sides round an accumulated value to bf16 and the GPU's fp32 MFMA
+sum runs in another order than the oracle's fp64 sum.
+
+Quantised activations: that one-ulp freedom in h can move an a2 value across a
+rounding boundary of its code, and a code step is a large change (1/8 of a value for
+e4m3, up to 1/2 for e2m1).  The gate is staged: stage-1 h within one ulp of the
+oracle's, the GPU's a2 codes bit-exactly equal to the oracle quantiser applied to the
+GPU's own h, and the output bound against the oracle's stage 2 fed the GPU's h.  The
+end-to-end result (oracle h, oracle a2) is reported with the count of differing a2 codes
+(asserted below 0.2%) under a per-row L2 of 2e-2 and max 0.1 * rms: measured on the
+full-size fp8-block workload (N(0, 1/K) weights quantised per 128x128 block), the FP8
+MFMA's 128-product sums leave 2.1% of h values one ulp from the oracle's fp64 result
+(bf16 MFMA paths: 0.1-0.2%), 0.17% of a2 codes then differ, and one such step in the
+shared expert's slot (weight 1) moves an output by up to ~4% of rms, so no implementation
+whose h differs from the oracle's in the last bit can hold 2e-2 * rms end to end there.
 """
 import numpy as np
 import pytest
 import torch
 
 from gpu_common import (B, DEV, bf16_dev, check_output, check_rounding, combine_f32, dev_weights, h_by_slot,
-                        layer_for, orc, run_layer, say, synth, tiled_reference, to_dev)
+                        layer_for, orc, run_layer, say, synth, targeted_tokens, tiled_reference, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,12 +101,11 @@ def full_check(w, data, res, tokens=None, what="", act=None):
     c_ref, _ = orc.quant_act(ref_h[valid], w.afmt)
     c_gpu, _ = orc.quant_act(h_gpu[valid], w.afmt)
     flips = int(np.count_nonzero(c_ref != c_gpu))
-    # one e4m3 code flip moves a row by about 0.125 / sqrt(I) (0.7% at I = 288): the end-to-end
-    # row bound allows for the few flips; the strict bound is the stage-2 check above
-    e2e = check_output(acc, ref, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)",
-                       max_rel=0.1, row_l2=2e-2)
     assert flips <= max(4, c_ref.size // 500), f"{what}: {flips} a2 code bytes differ"
-    return e2e
+    # each differing a2 code moves its row by one code step (module notes): the strict bound
+    # is the stage-2 check above
+    return check_output(acc, ref, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)",
+                        max_rel=0.1, row_l2=2e-2)
 
 
 SMALL = []
@@ -147,8 +154,9 @@ def oai_case(w, data, interleaved, bias, kind=1):
     act = dict(kind=kind, alpha=1.702, beta=1.0, limit=7.0, interleaved=interleaved)
     b1, b2 = synth.make_biases(w) if bias else (None, None)
     if interleaved:
+        s1 = data["w1_scale"]  # per-tensor scales ([E]) have no rows to permute
         data = dict(data, w1=synth.interleave_rows(data["w1"], w.I),
-                    w1_scale=synth.interleave_rows(data["w1_scale"], w.I))
+                    w1_scale=synth.interleave_rows(s1, w.I) if s1 is not None and s1.ndim > 1 else s1)
         b1 = synth.interleave_rows(b1, w.I) if b1 is not None else None
     act.update(w1_bias=b1, w2_bias=b2)
     return act, data
@@ -271,21 +279,15 @@ def test_single_token_all_slots_one_expert():
 
 
 # ---------------------------------------------------------------- full-size workloads
-def _sample(T, n, seed):
-    if T <= n:
-        return np.arange(T, dtype=np.int32)
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
-
-
-@pytest.mark.parametrize("name,n_tok,tiled", [("tiny", 64, False), ("decode", 64, False), ("decode", 64, True),
-                                              ("prefill", 24, False), ("prefill", 24, True)])
-def test_full_size_mxfp4_w4a16(name, n_tok, tiled):
+@pytest.mark.parametrize("name,tiled", [("tiny", False), ("decode", False), ("decode", True), ("prefill", False),
+                                        ("prefill", True)])
+def test_full_size_mxfp4_w4a16(name, tiled):
     w = synth.WORKLOADS[name]
     say(f"full-size {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.topk} tiled={tiled}")
     data = synth.make_all(w)
     res = run_layer(w, data, tiled=tiled)  # library-picked block_m, as the benchmark runs it
-    full_check(w, data, res, tokens=_sample(w.T, n_tok, 5), what=f"{name}/{'tiled' if tiled else 'canon'}")
+    tk = None if w.T <= 64 else targeted_tokens(res, w.T, w.K, n_min=32, seed=5)
+    full_check(w, data, res, tokens=tk, what=f"{name}/{'tiled' if tiled else 'canon'}")
 
 
 def test_full_size_prefill_w4a4():
@@ -296,7 +298,7 @@ def test_full_size_prefill_w4a4():
     # a1 codes are an integer product of the GPU quantiser: bit-exact on every token
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
-    full_check(w, data, res, tokens=_sample(w.T, 24, 6), what=w.name)
+    full_check(w, data, res, tokens=targeted_tokens(res, w.T, w.K, n_min=32, seed=6), what=w.name)
 
 
 def test_full_size_fp8_block_shared():
@@ -307,7 +309,9 @@ def test_full_size_fp8_block_shared():
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
     assert np.all(res["ids"][:, w.topk] == w.E) and np.all(res["weights"][:, w.topk] == 1.0)
-    full_check(w, data, res, tokens=_sample(w.T, 6, 7), what=w.name)
+    tk = targeted_tokens(res, w.T, w.K, n_min=16, seed=7)
+    say(f"{w.name}: {len(tk)} targeted tokens (last row block of each of {w.E_total} experts, hot and cold experts)")
+    full_check(w, data, res, tokens=tk, what=w.name)
 
 
 @pytest.fixture(scope="module")
@@ -325,7 +329,7 @@ def test_full_size_fp8_channel_sweep(fp8_channel_data, T):
     res = run_layer(w, data)
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
-    full_check(w, data, res, tokens=_sample(T, 6, 8), what=f"{w.name}/T{T}")
+    full_check(w, data, res, tokens=targeted_tokens(res, T, w.K, n_min=16, seed=8), what=f"{w.name}/T{T}")
 
 
 FP8T = (synth.W_FP8_TENSOR, synth.A_FP8_TENSOR)
@@ -342,3 +346,37 @@ def test_fp8_per_tensor(bm, tiled):
     res = run_layer(w, data, block_m=bm, tiled=tiled)
     assert res["a1_scales"].view(np.float32).size == 1
     full_check(w, data, res, what=f"fp8-tensor/bm{bm}/{'tiled' if tiled else 'canon'}")
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_fp8_per_tensor_with_biases(bm):
+    """Per-tensor FP8 with both projection biases and interleaved gate/up rows: pad rows of
+    h are written as 0, so the per-tensor a2 scale covers the routed rows only, as the
+    oracle's does (a pad row with act(bias) would raise the amax)."""
+    w = small(FP8T, T=33, H=320, I=416, E=4, k=2, seed=73)
+    data = synth.make_all(w)
+    act, data = oai_case(w, data, True, True, kind=1)
+    what = f"fp8-tensor/bm{bm}/itl/bias/oai"
+    say(f"forward {what}")
+    res = run_layer(w, data, block_m=bm, tiled=True, act=act)
+    npad = int(res["sort"]["num_padded"][0])
+    pad = res["sort"]["sorted_slots"][:npad] >= w.T * w.K
+    assert pad.any() and not res["h_sorted"][:npad][pad].any(), "pad rows of h must be 0"
+    full_check(w, data, res, what=what, act=act)
+
+
+UNIFORM = [(FP8B, 16), (FP8B, 64), (FP8C, 32), (FP8C, 64)]
+
+
+@pytest.mark.parametrize("fmt,bm", UNIFORM, ids=[f"w{f[0]}a{f[1]}-bm{bm}" for f, bm in UNIFORM])
+def test_small_fp8_uniform_codes(fmt, bm):
+    """FP8 weights drawn as uniform codes over [0.125, 1.875] with random fp32 scales (the
+    other weight generator), on the small shapes."""
+    if fmt == FP8B:
+        w = small(fmt, T=40, H=352, I=288, E=5, k=3, n_shared=1, score=synth.SCORE_SIGMOID, seed=13)
+    else:
+        w = small(fmt, T=33, H=320, I=416, E=4, k=2, seed=14)
+    w = w.scaled(fp8_weights="uniform")
+    data = synth.make_all(w)
+    res = run_layer(w, data, block_m=bm, tiled=True)
+    full_check(w, data, res, what=f"{w.name}/bm{bm}/uniform-codes")
