@@ -311,6 +311,24 @@ moe_status moe_workspace_layout(const moe_forward_args* a, moe_workspace_layout_
 moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_experts_forward_noalloc -- moe_experts_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, launches and results bit for bit, with the workspace
+ * taken from a scratch area the library owns instead of a->workspace (a->workspace and
+ * a->workspace_bytes are ignored).  The call allocates nothing, ever.
+ * The scratch is MOE_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory per device the
+ * library runs on, held until the process ends; it fits a call whose
+ * moe_experts_workspace_bytes() is at most that (e.g. the decode shapes: T = 64, H = I =
+ * 2880, 32 experts, top-4 need about 7 MB).  Larger calls return MOE_EWORKSPACE with
+ * nothing enqueued.  Every call on one device shares that device's scratch and leaves the
+ * last call's intermediates in it: calls that may overlap on one device (two streams, two
+ * host threads) race and must be ordered by the caller.  Arguments, limits and errors are
+ * otherwise those of moe_experts_forward.
+ * ---------------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_experts_forward_noalloc(const moe_forward_args* a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_layer_forward -- the whole layer from router logits: moe_route_align (E = E_total -
  * n_shared routed experts, topk = K - n_shared, the block_m of `a`) writing into the
  * routing buffers that `a` names, then moe_experts_forward(a).  The pages' layer takes

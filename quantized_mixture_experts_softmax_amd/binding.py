@@ -27,8 +27,10 @@ EXPORTED = [
     "moe_route_topk", "moe_route_grouped_topk", "moe_map_experts", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward", "moe_layer_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
-    "moe_tiled_weight_bytes", "moe_tile_weights",
+    "moe_tiled_weight_bytes", "moe_tile_weights", "moe_experts_forward_noalloc",
 ]
+# library-owned workspace of moe_experts_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 
 
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(ForwardArgs), ctypes.POINTER(WorkspaceLayout)]
         L.moe_experts_forward.restype = S
         L.moe_experts_forward.argtypes = [ctypes.POINTER(ForwardArgs), P]
+        L.moe_experts_forward_noalloc.restype = S
+        L.moe_experts_forward_noalloc.argtypes = [ctypes.POINTER(ForwardArgs), P]
         L.moe_layer_forward.restype = S
         L.moe_layer_forward.argtypes = [ctypes.POINTER(ForwardArgs), P, I, I, I, ctypes.c_float, P, P, P]
         L.moe_supports.restype = S
@@ -370,6 +374,23 @@ def moe_experts_forward(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, top
         args.workspace_bytes = workspace.numel()
     _check(lib().moe_experts_forward(ctypes.byref(args), _stream(stream, dev)))
     return out, workspace
+
+
+def moe_experts_forward_noalloc(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict,
+                                wfmt: int, afmt: int, block_m: int, E_total: int, I: int, out=None, a1_codes=None,
+                                a1_scales=None, stream=None, weight_layout: int = LAYOUT_CANONICAL,
+                                act: dict | None = None):
+    """moe_experts_forward with the workspace in the library's own scratch (no workspace
+    argument; see include/moe.h).  Returns out."""
+    dev = _dev(hidden_states)
+    assert hidden_states.dtype == torch.bfloat16
+    T, H = hidden_states.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    args = forward_args(hidden_states, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort, wfmt, afmt,
+                        block_m, E_total, I, out, None, a1_codes, a1_scales, weight_layout, act)
+    _check(lib().moe_experts_forward_noalloc(ctypes.byref(args), _stream(stream, dev)))
+    return out
 
 
 def moe_layer_forward(hidden_states, router_logits, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sort: dict,

@@ -4,8 +4,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
+
+// Workspace of moe_experts_forward_noalloc: device memory the library owns, one copy per
+// device (the code object's copy on that device), held until the process ends.  Host code
+// never names this array as an address: its device address comes from hipGetSymbolAddress
+// (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -473,12 +481,60 @@ moe_status experts_forward(const moe_forward_args* a, const FusedRoute* r, hipSt
   return hip_status(prof_mark(3, stream), "moe_experts_forward: profiling event");
 }
 
+// Device address of `scratch` on the current device: looked up once per device (with that
+// device current) and kept; NULL with the HIP error in *err when the lookup fails.
+void* scratch_ptr(hipError_t* err) {
+  static std::atomic<void*> ptrs[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev].store(p, std::memory_order_release);  // two threads racing store the same address
+  }
+  *err = hipSuccess;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
 
 moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   return experts_forward(a, nullptr, stream);
+}
+
+moe_status moe_experts_forward_noalloc(const moe_forward_args* a, hipStream_t stream) {
+  moe_status st = check_shapes(a);
+  if (st != MOE_OK) return st;
+  moe_forward_args c = *a;
+  c.workspace = nullptr;
+  c.workspace_bytes = 0;
+  moe_workspace_layout_t L;
+  if ((st = moe_workspace_layout(&c, &L)) != MOE_OK) return st;
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE, "moe_experts_forward_noalloc: this call needs a workspace of %zu bytes, more than "
+                                "the library's scratch of %zu bytes (use moe_experts_forward with a caller workspace)",
+                L.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  if (a->T == 0) return ok();
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws) return hip_status(e, "moe_experts_forward_noalloc: scratch address");
+  c.workspace = ws;
+  c.workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  return experts_forward(&c, nullptr, stream);
 }
 
 moe_status moe_layer_forward(const moe_forward_args* a, const float* router_logits, moe_score score, int renormalize,

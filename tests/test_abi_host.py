@@ -240,3 +240,18 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libmoe.so"))
     with pytest.raises(RuntimeError, match="libmoe.so not found"):
         B.moe_pick_block_m(64, 4, 32)
+
+
+def test_noalloc_rejects_oversize(lib):
+    """A call whose workspace exceeds the library's scratch is refused on the host, before
+    any HIP call (prefill shapes: T = 8192, H = I = 2880, 128 experts, top-4)."""
+    a = B.ForwardArgs()
+    a.T, a.H, a.I, a.E_total, a.K, a.block_m = 8192, 2880, 2880, 128, 4, 64
+    a.wfmt, a.afmt, a.act = B.W_MXFP4, B.A_BF16, B.ACT_SILU
+    need = lib.moe_experts_workspace_bytes(ctypes.byref(a))
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    st = lib.moe_experts_forward_noalloc(ctypes.byref(a), None)
+    assert st == B.MOE_EWORKSPACE
+    assert "scratch" in B.moe_last_error()
+    a.H = 100  # shape errors come first, as for moe_experts_forward
+    assert lib.moe_experts_forward_noalloc(ctypes.byref(a), None) == B.MOE_EINVAL
