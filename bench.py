@@ -18,6 +18,13 @@ events recorded on the launch stream around the stage-1 launch of every n-th tim
 (--event-every, default 10: each event record adds a few microseconds to its step, so
 the other steps run without them).
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+
+`extra_configs` (after the headline, --extra all): the prefill-sized workloads timed the
+same way with fewer steps -- prefill MXFP4 w4a16 and w4a4 (T=8192, E=128, top-4), FP8 block
+with a shared expert (T=4096, E=256+1, top-8+1) and the FP8 per-channel sweep (T = 1, 16,
+256, 4096) -- each with tokens/s, its step's fraction of the binding roofline (HBM or the
+path's MFMA peak, whichever bounds its algorithmic bytes and flops) and the stage-1 kernel
+time from events on one more step.
 """
 from __future__ import annotations
 
@@ -163,6 +170,103 @@ def cpu_baseline(w, data, seconds: float, act_host: dict | None = None, emap=Non
                       f"(fp64 per-token loop, OpenMP), {el:.1f} s"}
 
 
+WFMT_NAMES = ["mxfp4", "fp8-block128", "fp8-channel", "fp8-tensor", "bf16"]
+AFMT_NAMES = ["w4a16", "a-mxfp4", "a-fp8-g128", "a-fp8-token", "a-fp8-tensor"]
+
+
+def workload_label(w) -> str:
+    from quantized_mixture_experts_softmax_amd import synth
+
+    a = "a-bf16" if w.wfmt == synth.W_BF16 else AFMT_NAMES[w.afmt]
+    return f"{w.name}-{WFMT_NAMES[w.wfmt]}-{a}"
+
+
+def step_roofline(w, alg, ms: float) -> dict:
+    """The step's fraction of its binding roofline: algorithmic bytes at HBM peak against
+    algorithmic flops at the path's MFMA peak, whichever takes longer."""
+    dt = mfma_dtype(w)
+    t_hbm = alg["step_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["step_flops"] / (MFMA_PEAK_TFLOPS[dt] * 1e12)
+    s = ms * 1e-3
+    return {"bound": "hbm" if t_hbm >= t_mfma else f"mfma-{dt}", "frac": round(max(t_hbm, t_mfma) / s, 4),
+            "hbm_frac": round(t_hbm / s, 4), "mfma_frac": round(t_mfma / s, 4),
+            "achieved_gbs": round(alg["step_bytes"] / s / 1e9, 1), "achieved_tflops": round(alg["step_flops"] / s / 1e12, 1)}
+
+
+# (workload, token count) of the extra bench entries; the fp8-channel sweep takes prefixes
+# of one T = 4096 draw
+EXTRA_CONFIGS = [("prefill", None), ("prefill-w4a4", None), ("fp8-block", None), ("fp8-channel", 1),
+                 ("fp8-channel", 16), ("fp8-channel", 256), ("fp8-channel", 4096)]
+
+
+def measure_extra(steps: int, warmup: int, hip, dev) -> dict:
+    """Times each EXTRA_CONFIGS workload: tiled weights (rotated copies when one copy is
+    smaller than twice the Infinity Cache), plain top-k routing through MoELayer, `warmup`
+    untimed steps, `steps` timed steps between HIP events on the launch stream and wall
+    clock, then one step with the per-stage events."""
+    import numpy as np
+    import torch
+
+    from quantized_mixture_experts_softmax_amd import binding as B
+    from quantized_mixture_experts_softmax_amd import synth
+
+    out = {}
+    cache = {}
+    for name, T in EXTRA_CONFIGS:
+        w0 = synth.WORKLOADS[name]
+        if name not in cache:
+            cache.clear()
+            cache[name] = synth.make_all(w0)
+        full = cache[name]
+        w = w0.with_T(T) if T else w0
+        data = dict(full, x=full["x"][:w.T], logits=full["logits"][:w.T])
+        wbytes = sum(data[k].nbytes for k in ("w1", "w1_scale", "w2", "w2_scale") if data[k] is not None)
+        copies = 1 if wbytes >= 2 * MALL_BYTES else min(64, -(-2 * MALL_BYTES // wbytes) + 1)
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        layers = [B.MoELayer(t(data["w1"]), t(data["w1_scale"]), t(data["w2"]), t(data["w2_scale"]), H=w.H, I=w.I,
+                             E=w.E, topk=w.topk, wfmt=w.wfmt, afmt=w.afmt,
+                             score="softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid", n_shared=w.n_shared,
+                             shared_weight=w.shared_weight, tiled=True) for _ in range(copies)]
+        x = torch.from_numpy(np.ascontiguousarray(data["x"]).view(np.int16)).view(torch.bfloat16).to(dev)
+        logits = t(data["logits"])
+        for i in range(warmup):
+            layers[i % copies](x, logits)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        e0, e1 = _event(hip), _event(hip)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hip.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
+        for i in range(steps):
+            layers[i % copies](x, logits)
+        hip.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        gpu_ms = _elapsed_ms(hip, e0, e1) / steps
+        ev = [_event(hip) for _ in range(4)]
+        B.moe_profile_events(ev)
+        layers[0](x, logits)
+        B.moe_profile_events(None)
+        torch.cuda.synchronize()
+        g1 = _elapsed_ms(hip, ev[0], ev[1])
+        b = layers[0]._bufs[(w.T, str(dev))]
+        alg = algorithmic(w, b["ids"].cpu().numpy())
+        label = workload_label(w) + (f"-T{w.T}" if T else "")
+        out[label] = {
+            "T": w.T, "steps": steps, "ms_per_step": round(wall_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5),
+            "tokens_per_s": round(w.T / (wall_ms * 1e-3), 1), "block_m": b["bm"], "weight_copies": copies,
+            "experts_hit": alg["n_hit"], "roofline": step_roofline(w, alg, wall_ms),
+            "stage_us": {"stage1_gemm": round(g1 * 1e3, 2),
+                         "a2_quant+stage2_gemm": round(_elapsed_ms(hip, ev[1], ev[2]) * 1e3, 2),
+                         "combine": round(_elapsed_ms(hip, ev[2], ev[3]) * 1e3, 2)},
+        }
+        del layers, x, logits, b
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        print(f"bench.py: {label}: {wall_ms:.4f} ms/step, {out[label]['roofline']['frac']:.3f} of the "
+              f"{out[label]['roofline']['bound']} roof", file=sys.stderr, flush=True)
+    return out
+
+
 def main() -> int:
     from quantized_mixture_experts_softmax_amd import synth
 
@@ -193,6 +297,10 @@ def main() -> int:
                     help="record the per-stage HIP events on every n-th timed step (each record adds a few us)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--extra", choices=["all", "none"], default="all",
+                    help="all: also time the prefill-sized workloads and the fp8-channel sweep (extra_configs)")
+    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--extra-warmup", type=int, default=3)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -341,8 +449,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic (seeded; random weight codes and scales, no checkpoint)",
-        "config": {"workload": f"{w.name}-{['mxfp4', 'fp8-block128', 'fp8-channel', 'fp8-tensor', 'bf16'][w.wfmt]}-"
-                               f"{['a-bf16' if w.wfmt == synth.W_BF16 else 'w4a16', 'a-mxfp4', 'a-fp8-g128', 'a-fp8-token', 'a-fp8-tensor'][w.afmt]}",
+        "config": {"workload": workload_label(w),
                    "T": w.T, "H": w.H, "I": w.I, "experts": w.E, "shared_experts": w.n_shared, "topk": w.topk,
                    "router": "softmax" if w.score == synth.SCORE_SOFTMAX else "sigmoid",
                    "block_m": b["bm"], "weight_copies": copies, "experts_hit": alg["n_hit"],
@@ -367,6 +474,11 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = n
+    if args.extra == "all":
+        del layers
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["extra_configs"] = measure_extra(args.extra_steps, args.extra_warmup, hip, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds, act_host,
                                               None if emap is None else emap.cpu().numpy())
