@@ -113,7 +113,8 @@ def mfma_dtype(w):
 # Sources compiled into the grouped-GEMM kernels (the route + sort fused into stage 1
 # comes from sort_device.h, which includes route_device.h): a counter summary is current
 # only for these bytes.
-GEMM_SOURCES = ("experts_gemm.hip", "moe_device.h", "moe_internal.h", "sort_device.h", "route_device.h")
+GEMM_SOURCES = ("experts_gemm.hip", "gemm_lds.hip", "gemm_common.h", "moe_device.h", "moe_internal.h", "sort_device.h",
+                "route_device.h")
 
 
 def gemm_source_sha() -> str:

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["route_topk.hip", "route_grouped.hip", "align_sort.hip", "expert_map.hip", "quant_act.hip", "experts_gemm.hip", "moe_abi.hip"]
+SOURCES = ["route_topk.hip", "route_grouped.hip", "align_sort.hip", "expert_map.hip", "quant_act.hip", "experts_gemm.hip", "gemm_lds.hip", "moe_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -120,6 +120,9 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
 hipError_t launch_tile_weights(int wfmt, int E, int N, int K, const uint8_t* w, const void* ws, uint8_t* out,
                                hipStream_t stream);
 hipError_t launch_gemm(int stage, int wfmt, int afmt, int block_m, const GemmParams& p, hipStream_t stream);
+// 128-row blocks on tiled weights with both operands staged in LDS (gemm_lds.hip); epi: the
+// general epilogue (biases, SwiGLU-OAI, interleaved rows, router weight on the input).
+hipError_t launch_gemm_lds(int stage, int wfmt, int afmt, int epi, const GemmParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* ybuf, const int32_t* topk_ids, const float* topk_weights, int T, int K,
                           int H, int E_total, uint16_t* out, hipStream_t stream);
 
