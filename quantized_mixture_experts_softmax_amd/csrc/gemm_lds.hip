@@ -39,12 +39,16 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128;     // rows per block
-constexpr int kWaves = 8;    // 2 row groups x 4 column groups
 constexpr int kNT = 4;       // 16-column weight tiles per wave
-constexpr int kTiles = 16;   // weight tiles per workgroup
-constexpr int kStages = 3;   // chunk buffers in the ring
 
-template <int AF>
+#ifndef MOE_LDS_WN      // column groups per workgroup (waves = 2 x column groups)
+#define MOE_LDS_WN 4
+#endif
+#ifndef MOE_LDS_STAGES  // chunk buffers in the ring
+#define MOE_LDS_STAGES 3
+#endif
+
+template <int AF, int kWaves>
 struct ATile {
   static constexpr int ARB = AF == kABf16 ? 256 : (AF == kAMxfp4 ? 64 : 128);  // bytes per row and chunk
   static constexpr int APC = ARB / 16;                                           // 16-byte units per row
@@ -58,20 +62,21 @@ struct ATile {
   __device__ static int swz(int r) { return (r / RPB) & (APC - 1); }
 };
 
-template <int WF>
+template <int WF, int kTiles>
 struct BTile {
   static constexpr int kBlock = WF == kWMxfp4 ? 1088 : 2048;
-  static constexpr int kBytes = kTiles * kBlock;
+  // MXFP4: the tiles' codes, then their 64-byte scale parts in one 1 KB run
+  static constexpr int kBytes = WF == kWMxfp4 ? kTiles * 1024 + 1024 : kTiles * kBlock;
 };
 
-template <int WF, int AF>
+template <int WF, int AF, int WN, int S>
 struct LdsStage {
   static constexpr int kA = 0;
-  static constexpr int kAs = ATile<AF>::kBytes;
-  static constexpr int kB = kAs + ATile<AF>::kScaleBytes;
-  static constexpr int kBytes = kB + BTile<WF>::kBytes;
+  static constexpr int kAs = ATile<AF, 2 * WN>::kBytes;
+  static constexpr int kB = kAs + ATile<AF, 2 * WN>::kScaleBytes;
+  static constexpr int kBytes = kB + BTile<WF, 4 * WN>::kBytes;
   // after the ring: the per-row FP8 token scales (loaded once)
-  static constexpr int kRing = kStages * kBytes;
+  static constexpr int kRing = S * kBytes;
   static constexpr int kTotal = kRing + (AF == kAFp8Token ? kBM * 4 : 0);
 };
 
@@ -99,12 +104,13 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 }  // namespace
 
-template <int STAGE, int WF, int AF, int EPI>
-__global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p) {
-  using AT = ATile<AF>;
-  using BT = BTile<WF>;
-  using LS = LdsStage<WF, AF>;
-  constexpr int COLS_PER_WG = (STAGE == 1) ? 8 * kNT * 4 : 16 * kNT * 4;  // 128 (gate/up pairs) or 256
+template <int STAGE, int WF, int AF, int EPI, int WN, int kStages>
+__global__ __launch_bounds__(128 * WN, 1) void moe_gemm_lds_kernel(const GemmParams p) {
+  constexpr int kWaves = 2 * WN, kTiles = 4 * WN;  // 2 row groups x WN column groups; 4 tiles per column group
+  using AT = ATile<AF, kWaves>;
+  using BT = BTile<WF, kTiles>;
+  using LS = LdsStage<WF, AF, WN, kStages>;
+  constexpr int COLS_PER_WG = (STAGE == 1) ? 8 * kNT * WN : 16 * kNT * WN;  // gate/up pairs, or output columns
   constexpr int ARB = AT::ARB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -121,6 +127,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p
   const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;  // row group (64 rows), column group (4 tiles)
+  static_assert(kTiles == 2 * kWaves, "each wave moves two weight tiles");
   const int K = p.K, nch = (K + 127) / 128;
   const int TK = p.T * p.slots_per_token;
   const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
@@ -157,14 +164,14 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p
     b_ok[q] = ok;
     b_src[q] = p.w + ((size_t)e * p.Nw + trow) / 16 * (size_t)nch * BT::kBlock;
   }
-  // MXFP4: wave 0 moves the 16 tiles' 64-byte scale parts with one 16-byte-per-lane load
-  // (lane l: tile l / 4, bytes [16 (l % 4), +16))
+  // MXFP4: wave 0 moves the tiles' 64-byte scale parts with one 16-byte-per-lane load
+  // (lane l: tile l / 4, bytes [16 (l % 4), +16); lanes past the last tile read zeros)
   const uint8_t* bs_src = nullptr;
   bool bs_ok = false;
   if constexpr (WF == kWMxfp4) {
     bool ok;
-    const int trow = tile_row(lane >> 2, ok);
-    bs_ok = ok;
+    const int trow = tile_row((lane >> 2) < kTiles ? lane >> 2 : 0, ok);
+    bs_ok = ok && (lane >> 2) < kTiles;
     bs_src = p.w + ((size_t)e * p.Nw + trow) / 16 * (size_t)nch * BT::kBlock + 1024 + 16 * (lane & 3);
   }
 
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p
                   (WF == kWMxfp4 && w == 0 ? 1 : 0);
   // MXFP4 activations: the E8M0 bytes of chunk c + 1 are loaded into registers at chunk c,
   // before chunk c + 2's direct loads, so the wait for chunk c + 1 covers them (three buffers)
-  static_assert(AF != kAMxfp4 || kStages == 3, "the activation scale bytes run one chunk ahead");
+  static_assert(AF != kAMxfp4 || kStages <= 3, "the activation scale bytes run one chunk ahead");
 
   // Issues the direct loads of chunk c into ring buffer c % kStages (chunks past the end
   // read the zero page, so every chunk costs the same operations).
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p
       if (w == 0) {
         const bool ok = live && bs_ok;
         const MOE_GLOBAL uint8_t* src = ok ? (const MOE_GLOBAL uint8_t*)bs_src + (size_t)c * BT::kBlock : zp;
-        dma16((const void*)src, st + LS::kB + kTiles * 1024);  // scale parts packed after the 16 data parts
+        dma16((const void*)src, st + LS::kB + kTiles * 1024);  // scale parts packed after the tiles' codes
       }
     }
     if constexpr (AF == kAFp8G128) {
@@ -502,9 +509,10 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_lds_kernel(const GemmParams p
 
 template <int STAGE, int WF, int AF, int EPI>
 static hipError_t launch_lds_impl(const GemmParams& p, hipStream_t stream) {
-  using LS = LdsStage<WF, AF>;
-  constexpr int COLS_PER_WG = (STAGE == 1) ? 8 * kNT * 4 : 16 * kNT * 4;
-  auto kern = moe_gemm_lds_kernel<STAGE, WF, AF, EPI>;
+  constexpr int WN = MOE_LDS_WN, S = MOE_LDS_STAGES;
+  using LS = LdsStage<WF, AF, WN, S>;
+  constexpr int COLS_PER_WG = (STAGE == 1) ? 8 * kNT * WN : 16 * kNT * WN;
+  auto kern = moe_gemm_lds_kernel<STAGE, WF, AF, EPI, WN, S>;
   static std::atomic<bool> attr_set[64];
   int dev = 0;
   const bool cached = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
@@ -517,7 +525,7 @@ static hipError_t launch_lds_impl(const GemmParams& p, hipStream_t stream) {
   const long G = (long)p.num_blocks * n_tiles;
   if (G == 0) return hipSuccess;
   if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  kern<<<(unsigned)G, 64 * kWaves, LS::kTotal, stream>>>(p);
+  kern<<<(unsigned)G, 128 * WN, LS::kTotal, stream>>>(p);
   return hipGetLastError();
 }
 
