@@ -182,6 +182,30 @@ def workload_label(w) -> str:
     return f"{w.name}-{WFMT_NAMES[w.wfmt]}-{a}"
 
 
+def stage1_roofline(w, alg, g1_ms: float, profile_name: str, launches: int) -> dict:
+    """The stage-1 GEMM (the dominant kernel) against its binding roof: algorithmic bytes per
+    launch at HBM peak or algorithmic flops at the path's MFMA peak, whichever takes longer,
+    divided by the launch's event-timed duration; traffic from the committed counter summary of
+    this workload when it was taken on the current kernel sources (else null)."""
+    dt = mfma_dtype(w)
+    t_hbm = alg["gemm1_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["gemm1_flops"] / (MFMA_PEAK_TFLOPS[dt] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = alg["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg["gemm1_flops"] / (g1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4)}
+    roof["traffic"] = traffic_from_profiles(profile_name)
+    roof["alg_bytes_per_launch"] = alg["gemm1_bytes"]
+    roof["alg_flops_per_launch"] = alg["gemm1_flops"]
+    roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
+    roof["launches_timed"] = launches
+    return roof
+
+
 def step_roofline(w, alg, ms: float) -> dict:
     """The step's fraction of its binding roofline: algorithmic bytes at HBM peak against
     algorithmic flops at the path's MFMA peak, whichever takes longer."""
@@ -243,12 +267,15 @@ def measure_extra(steps: int, warmup: int, hip, dev) -> dict:
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
         gpu_ms = _elapsed_ms(hip, e0, e1) / steps
-        ev = [_event(hip) for _ in range(4)]
-        B.moe_profile_events(ev)
-        layers[0](x, logits)
-        B.moe_profile_events(None)
+        # per-stage events on three more steps (each record adds a few microseconds)
+        evs = [[_event(hip) for _ in range(4)] for _ in range(3)]
+        for i, ev in enumerate(evs):
+            B.moe_profile_events(ev)
+            layers[i % copies](x, logits)
+            B.moe_profile_events(None)
         torch.cuda.synchronize()
-        g1 = _elapsed_ms(hip, ev[0], ev[1])
+        ev = evs[-1]
+        g1 = sum(_elapsed_ms(hip, e[0], e[1]) for e in evs) / len(evs)
         b = layers[0]._bufs[(w.T, str(dev))]
         alg = algorithmic(w, b["ids"].cpu().numpy())
         label = workload_label(w) + (f"-T{w.T}" if T else "")
@@ -256,6 +283,7 @@ def measure_extra(steps: int, warmup: int, hip, dev) -> dict:
             "T": w.T, "steps": steps, "ms_per_step": round(wall_ms, 5), "gpu_ms_per_step": round(gpu_ms, 5),
             "tokens_per_s": round(w.T / (wall_ms * 1e-3), 1), "block_m": b["bm"], "weight_copies": copies,
             "experts_hit": alg["n_hit"], "roofline": step_roofline(w, alg, wall_ms),
+            "stage1_roofline": stage1_roofline(w, alg, g1, w.name + (f"-T{w.T}" if T else ""), len(evs)),
             "stage_us": {"stage1_gemm": round(g1 * 1e3, 2),
                          "a2_quant+stage2_gemm": round(_elapsed_ms(hip, ev[1], ev[2]) * 1e3, 2),
                          "combine": round(_elapsed_ms(hip, ev[2], ev[3]) * 1e3, 2)},
@@ -417,25 +445,11 @@ def main() -> int:
     alg = algorithmic(w, ids_np)
     g1_ms = float(np.mean(g1))
     dt = mfma_dtype(w)
-    t_hbm = alg["gemm1_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = alg["gemm1_flops"] / (MFMA_PEAK_TFLOPS[dt] * 1e12)
-    if t_hbm >= t_mfma:
-        achieved = alg["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = alg["gemm1_flops"] / (g1_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4)}
-    traffic = traffic_from_profiles(w.name if not args.tokens else f"{w.name}-T{w.T}")
-    roof["traffic"] = traffic
+    roof = stage1_roofline(w, alg, g1_ms, w.name if not args.tokens else f"{w.name}-T{w.T}", len(evs))
     roof["kernel"] = ("stage-1 grouped GEMM (gate/up + SiLU-and-mul): "
                       + ("moe_gemm_persist_kernel" if b["bm"] == 16 else
-                         "moe_gemm_ksplit_kernel" if b["bm"] == 32 else "moe_gemm_kernel"))
-    roof["alg_bytes_per_launch"] = alg["gemm1_bytes"]
-    roof["alg_flops_per_launch"] = alg["gemm1_flops"]
-    roof["avg_launch_us"] = round(g1_ms * 1e3, 2)
-    roof["launches_timed"] = len(evs)
+                         "moe_gemm_ksplit_kernel" if b["bm"] == 32 else
+                         "moe_gemm_lds_kernel" if b["bm"] == 128 and args.layout == "tiled" else "moe_gemm_kernel"))
 
     result = {
         "metric": METRIC,
