@@ -1534,6 +1534,23 @@ static hipError_t launch_persist(const GemmParams& p, size_t lds, hipStream_t st
   return hipGetLastError();
 }
 
+// Small-block launch: strips per workgroup so that the grid is about
+// MOE_KSPLIT_WGS_PER_CU workgroups for each of the 256 CUs, at least one strip each.
+template <int STAGE, int WF, int AF, int BM, int NT, int WL, int EPI>
+static hipError_t launch_ksplit(const GemmParams& p_in, hipStream_t stream) {
+  constexpr int COLS_PER_STRIP = (STAGE == 1) ? 8 * NT : 16 * NT;
+  GemmParams p = p_in;
+  const long n_tiles = (p.N + COLS_PER_STRIP - 1) / COLS_PER_STRIP;
+  const long items = (long)p.num_blocks * n_tiles;
+  const long target = 256L * MOE_KSPLIT_WGS_PER_CU;
+  p.strips_per_wg = (int)std::max(1L, std::min(n_tiles, items / target));
+  const long G = (long)p.num_blocks * ((n_tiles + p.strips_per_wg - 1) / p.strips_per_wg);
+  if (G == 0) return hipSuccess;
+  if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
+  moe_gemm_ksplit_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <int STAGE, int WF, int AF, int BM, int WL, int EPI>
 static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   if constexpr (BM == 16) {
@@ -1565,26 +1582,26 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   } else {
   // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : (WF == kWBf16 ? 2 : 4);
-  constexpr int COLS_PER_WG = kSplit ? ((STAGE == 1) ? 8 * NT : 16 * NT) : ((STAGE == 1) ? 32 * NT : 64 * NT);
-  GemmParams p = p_in;
-  const long n_tiles = (p.N + COLS_PER_WG - 1) / COLS_PER_WG;
-  long groups = n_tiles;
   if constexpr (kSplit) {
-    // strips per workgroup: about MOE_KSPLIT_WAVES_PER_CU resident workgroups' worth
-    // of (block, strip) items for each of the 256 CUs, at least one strip each
-    const long items = (long)p.num_blocks * n_tiles;
+    // Stage 2 with few row blocks (one or two tokens): narrower strips, so that the
+    // grid still covers every CU, down to one tile per wave
     const long target = 256L * MOE_KSPLIT_WGS_PER_CU;
-    p.strips_per_wg = (int)std::max(1L, std::min(n_tiles, items / target));
-    groups = (n_tiles + p.strips_per_wg - 1) / p.strips_per_wg;
-  }
-  const long G = (long)p.num_blocks * groups;
+    if constexpr (STAGE == 2 && NT >= 4) {
+      if ((long)p_in.num_blocks * ((p_in.N + 16 * NT - 1) / (16 * NT)) < target) {
+        if ((long)p_in.num_blocks * ((p_in.N + 32 - 1) / 32) >= target)
+          return launch_ksplit<STAGE, WF, AF, BM, 2, WL, EPI>(p_in, stream);
+        return launch_ksplit<STAGE, WF, AF, BM, 1, WL, EPI>(p_in, stream);
+      }
+    }
+    return launch_ksplit<STAGE, WF, AF, BM, NT, WL, EPI>(p_in, stream);
+  } else {
+  constexpr int COLS_PER_WG = (STAGE == 1) ? 32 * NT : 64 * NT;
+  const long G = (long)p_in.num_blocks * ((p_in.N + COLS_PER_WG - 1) / COLS_PER_WG);
   if (G == 0) return hipSuccess;
   if (G > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  if constexpr (kSplit)
-    moe_gemm_ksplit_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
-  else
-    moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p);
+  moe_gemm_kernel<STAGE, WF, AF, BM, NT, WL, EPI><<<(unsigned)G, 256, 0, stream>>>(p_in);
   return hipGetLastError();
+  }
   }
 }
 

@@ -65,29 +65,35 @@ __global__ __launch_bounds__(256) void quant_fp8_g128_kernel(const uint16_t* __r
   if (live && sub == 0) scales[(size_t)r * ng + g] = s;
 }
 
-// FP8, one scale per row: one 256-thread workgroup per row.
-__global__ __launch_bounds__(256) void quant_fp8_token_kernel(const uint16_t* __restrict__ x, int rows, int cols,
-                                                              const int32_t* __restrict__ rows_dev,
-                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
+// FP8, one scale per row: one workgroup of NT threads per row; a thread keeps its up to
+// 8 * CH values in registers between the row maximum and the encoding (cols <= 8 * CH * NT).
+template <int NT, int CH>
+__global__ __launch_bounds__(NT) void quant_fp8_token_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                             const int32_t* __restrict__ rows_dev,
+                                                             uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int r = blockIdx.x;
   if (rows_dev && r >= rows_dev[0]) return;
-  __shared__ float red[4];
+  __shared__ float red[NT / kWave];
   const uint16_t* xr = x + (size_t)r * cols;
+  float f[CH][8];
   float m = 0.0f;
-  for (int c = 8 * (int)threadIdx.x; c < cols; c += 2048) {  // cols % 32 == 0
-    float f[8];
-    load8_bf16(xr + c, true, f);
-    m = fmaxf(m, amax8(f));
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {  // cols % 32 == 0: eight columns are all in or all out
+    const int c = 8 * ((int)threadIdx.x + NT * i);
+    load8_bf16(xr + c, c < cols, f[i]);
+    m = fmaxf(m, amax8(f[i]));
   }
   m = wave_max(m);
   if (lane_id() == 0) red[threadIdx.x / kWave] = m;
   __syncthreads();
-  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float amax = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) amax = fmaxf(amax, red[i]);
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  for (int c = 8 * (int)threadIdx.x; c < cols; c += 2048) {
-    float f[8];
-    load8_bf16(xr + c, true, f);
-    *(uint2*)(codes + (size_t)r * cols + c) = e4m3_pack8(f, s);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = 8 * ((int)threadIdx.x + NT * i);
+    if (c < cols) *(uint2*)(codes + (size_t)r * cols + c) = e4m3_pack8(f[i], s);
   }
   if (threadIdx.x == 0) scales[r] = s;
 }
@@ -183,7 +189,12 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
     quant_fp8_g128_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
                                                                                 (float*)scales);
   } else if (fmt == kAFp8Token) {
-    quant_fp8_token_kernel<<<(unsigned)rows, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, (float*)scales);
+    // rows up to 2048 columns: 256 threads; wider rows (up to 65536): 1024 threads
+    if (cols <= 2048)
+      quant_fp8_token_kernel<256, 1><<<(unsigned)rows, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, (float*)scales);
+    else
+      quant_fp8_token_kernel<1024, 8><<<(unsigned)rows, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes,
+                                                                          (float*)scales);
   } else {
     const long octs = (long)rows * (cols / 8);
     quant_mxfp4_kernel<<<(unsigned)((octs + 255) / 256), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,

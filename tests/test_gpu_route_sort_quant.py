@@ -153,7 +153,11 @@ QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8
                # eight columns per lane: a row narrower than one pass of the workgroup, an
                # odd number of 32-groups, and a last 128-group half full
                ("fp8-token-narrow", B.A_FP8_TOKEN, 5, 96), ("mxfp4-odd-groups", B.A_MXFP4_G32, 9, 96),
-               ("fp8-g128-half-group", B.A_FP8_G128, 7, 2880), ("fp8-tensor-narrow", B.A_FP8_TENSOR, 3, 96)]
+               ("fp8-g128-half-group", B.A_FP8_G128, 7, 2880), ("fp8-tensor-narrow", B.A_FP8_TENSOR, 3, 96),
+               # per-token FP8: the widest row of the 256-thread kernel, the narrowest and
+               # the widest of the 1024-thread one
+               ("fp8-token-2048", B.A_FP8_TOKEN, 4, 2048), ("fp8-token-2080", B.A_FP8_TOKEN, 4, 2080),
+               ("fp8-token-max", B.A_FP8_TOKEN, 3, 65536)]
 
 
 @pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
