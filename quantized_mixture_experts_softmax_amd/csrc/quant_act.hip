@@ -42,27 +42,40 @@ __device__ __forceinline__ uint2 e4m3_pack8(const float (&f)[8], float s) {
   return make_uint2(lo, hi);
 }
 
-// FP8, 128-column groups: 16 lanes per (row, group), eight columns (16 bytes) per lane.
-// Every lane takes part in the group reduction (no early return before the shuffles).
+// FP8, 128-column groups: 16 lanes per (row, group), eight columns (16 bytes) per lane;
+// a workgroup takes U runs of 16 consecutive groups and issues all U loads of a lane
+// before the first reduction, so U loads per lane are in flight.  Every lane takes part
+// in the group reductions (no early return before the shuffles).
+template <int U>
 __global__ __launch_bounds__(256) void quant_fp8_g128_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                              const int32_t* __restrict__ rows_dev,
                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int ng = (cols + 127) / 128;
-  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const int sub = (int)(threadIdx.x & 15);
-  const bool in = gid < (long)rows * ng;
-  const int r = in ? (int)(gid / ng) : 0, g = in ? (int)(gid % ng) : 0;
-  const bool live = in && !(rows_dev && r >= rows_dev[0]);
-  const int c = g * 128 + 8 * sub;
-  const bool ok = live && c < cols;  // cols % 32 == 0: eight columns are all in or all out
-  float f[8];
-  load8_bf16(x + (size_t)r * cols + c, ok, f);
-  float m = amax8(f);
+  const int n_rows = rows_dev ? min(rows, rows_dev[0]) : rows;
+  float f[U][8];
+  int r[U], c[U], gi[U];
+  bool live[U], ok[U];
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  const float s = m > 0.0f ? m / 448.0f : 1.0f;
-  if (ok) *(uint2*)(codes + (size_t)r * cols + c) = e4m3_pack8(f, s);
-  if (live && sub == 0) scales[(size_t)r * ng + g] = s;
+  for (int u = 0; u < U; ++u) {
+    const long gid = ((long)blockIdx.x * U + u) * 16 + (threadIdx.x >> 4);
+    const bool in = gid < (long)rows * ng;
+    r[u] = in ? (int)(gid / ng) : 0;
+    gi[u] = in ? (int)(gid % ng) : 0;
+    live[u] = in && r[u] < n_rows;
+    c[u] = gi[u] * 128 + 8 * sub;
+    ok[u] = live[u] && c[u] < cols;  // cols % 32 == 0: eight columns are all in or all out
+    load8_bf16(x + (size_t)r[u] * cols + c[u], ok[u], f[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float m = amax8(f[u]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    const float s = m > 0.0f ? m / 448.0f : 1.0f;
+    if (ok[u]) *(uint2*)(codes + (size_t)r[u] * cols + c[u]) = e4m3_pack8(f[u], s);
+    if (live[u] && sub == 0) scales[(size_t)r[u] * ng + gi[u]] = s;
+  }
 }
 
 // FP8, one scale per row: one workgroup of NT threads per row; a thread keeps its up to
@@ -99,31 +112,41 @@ __global__ __launch_bounds__(NT) void quant_fp8_token_kernel(const uint16_t* __r
 }
 
 // MXFP4, 32-column groups: 4 lanes per group, eight columns (16 bytes in, 4 code bytes
-// out) per lane.
+// out) per lane; a workgroup takes U runs of 256 lanes' columns, all U loads issued first.
+template <int U>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                           const int32_t* __restrict__ rows_dev,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const long per_row = cols / 8;
-  const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;  // index of 8 consecutive columns
-  const bool in = q < (long)rows * per_row;
-  const int r = in ? (int)(q / per_row) : 0;
-  const int c = in ? (int)(q % per_row) * 8 : 0;
-  const bool live = in && !(rows_dev && r >= rows_dev[0]);
-  float f[8];
-  load8_bf16(x + (size_t)r * cols + c, live, f);
-  float m = amax8(f);
-  // groups are 4 consecutive lanes (cols % 32 == 0 keeps groups inside one row)
-  m = fmaxf(m, __shfl_xor(m, 2, kWave));
-  m = fmaxf(m, __shfl_xor(m, 1, kWave));
-  const int es = mx_shared_exp(m);
-  const float inv = exp2i(-es);
-  if (live) {
-    uint32_t packed = 0;
+  const int n_rows = rows_dev ? min(rows, rows_dev[0]) : rows;
+  float f[U][8];
+  int r[U], c[U];
+  bool live[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      packed |= (e2m1_encode(f[2 * i] * inv) | (e2m1_encode(f[2 * i + 1] * inv) << 4)) << (8 * i);
-    *(uint32_t*)(codes + (size_t)r * (cols / 2) + c / 2) = packed;
-    if ((c & 31) == 0) scales[(size_t)r * (cols / 32) + c / 32] = (uint8_t)(es + 127);
+  for (int u = 0; u < U; ++u) {
+    const long q = ((long)blockIdx.x * U + u) * 256 + threadIdx.x;  // index of 8 consecutive columns
+    const bool in = q < (long)rows * per_row;
+    r[u] = in ? (int)(q / per_row) : 0;
+    c[u] = in ? (int)(q % per_row) * 8 : 0;
+    live[u] = in && r[u] < n_rows;
+    load8_bf16(x + (size_t)r[u] * cols + c[u], live[u], f[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float m = amax8(f[u]);
+    // groups are 4 consecutive lanes (cols % 32 == 0 keeps groups inside one row)
+    m = fmaxf(m, __shfl_xor(m, 2, kWave));
+    m = fmaxf(m, __shfl_xor(m, 1, kWave));
+    const int es = mx_shared_exp(m);
+    const float inv = exp2i(-es);
+    if (live[u]) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        packed |= (e2m1_encode(f[u][2 * i] * inv) | (e2m1_encode(f[u][2 * i + 1] * inv) << 4)) << (8 * i);
+      *(uint32_t*)(codes + (size_t)r[u] * (cols / 2) + c[u] / 2) = packed;
+      if ((c[u] & 31) == 0) scales[(size_t)r[u] * (cols / 32) + c[u] / 32] = (uint8_t)(es + 127);
+    }
   }
 }
 
@@ -184,21 +207,28 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
     tensor_scale_final_kernel<<<1, 1, 0, stream>>>(acc);
     return hipGetLastError();
   }
+  constexpr int U = 4;  // loads in flight per lane in the group quantisers
   if (fmt == kAFp8G128) {
-    const long groups = (long)rows * ((cols + 127) / 128);  // 16 per 256-thread workgroup
-    quant_fp8_g128_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
-                                                                                (float*)scales);
+    const long groups = (long)rows * ((cols + 127) / 128);  // 16 U per 256-thread workgroup
+    quant_fp8_g128_kernel<U><<<(unsigned)((groups + 16 * U - 1) / (16 * U)), 256, 0, stream>>>(x, rows, cols, rows_dev,
+                                                                                              codes, (float*)scales);
   } else if (fmt == kAFp8Token) {
-    // rows up to 2048 columns: 256 threads; wider rows (up to 65536): 1024 threads
-    if (cols <= 2048)
-      quant_fp8_token_kernel<256, 1><<<(unsigned)rows, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, (float*)scales);
-    else
-      quant_fp8_token_kernel<1024, 8><<<(unsigned)rows, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes,
-                                                                          (float*)scales);
+    // one workgroup per row; the smallest of these shapes that holds the row, so that a
+    // thread has several 16-byte loads in flight: 256 threads x 1..8 octets (up to 16384
+    // columns), then 512 and 1024 threads x 8 octets (up to 65536)
+    const int oct = cols / 8;
+    float* sc = (float*)scales;
+    const unsigned R = (unsigned)rows;
+    if (oct <= 256) quant_fp8_token_kernel<256, 1><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    else if (oct <= 512) quant_fp8_token_kernel<256, 2><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    else if (oct <= 1024) quant_fp8_token_kernel<256, 4><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    else if (oct <= 2048) quant_fp8_token_kernel<256, 8><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    else if (oct <= 4096) quant_fp8_token_kernel<512, 8><<<R, 512, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    else quant_fp8_token_kernel<1024, 8><<<R, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
   } else {
     const long octs = (long)rows * (cols / 8);
-    quant_mxfp4_kernel<<<(unsigned)((octs + 255) / 256), 256, 0, stream>>>(x, rows, cols, rows_dev, codes,
-                                                                            (uint8_t*)scales);
+    quant_mxfp4_kernel<U><<<(unsigned)((octs + 256 * U - 1) / (256 * U)), 256, 0, stream>>>(x, rows, cols, rows_dev,
+                                                                                           codes, (uint8_t*)scales);
   }
   return hipGetLastError();
 }

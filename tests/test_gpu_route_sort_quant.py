@@ -157,7 +157,11 @@ QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8
                # per-token FP8: the widest row of the 256-thread kernel, the narrowest and
                # the widest of the 1024-thread one
                ("fp8-token-2048", B.A_FP8_TOKEN, 4, 2048), ("fp8-token-2080", B.A_FP8_TOKEN, 4, 2080),
-               ("fp8-token-max", B.A_FP8_TOKEN, 3, 65536)]
+               ("fp8-token-16416", B.A_FP8_TOKEN, 2, 16416), ("fp8-token-32768", B.A_FP8_TOKEN, 2, 32768),
+               ("fp8-token-max", B.A_FP8_TOKEN, 3, 65536),
+               # the group quantisers take 4 runs of lanes per workgroup: a grid whose last
+               # workgroup is partly past the end
+               ("fp8-g128-runs", B.A_FP8_G128, 65, 384), ("mxfp4-runs", B.A_MXFP4_G32, 37, 224)]
 
 
 @pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
