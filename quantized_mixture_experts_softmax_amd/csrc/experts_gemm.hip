@@ -341,10 +341,20 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
         const i32x4 hi = kDmaA ? *(const i32x4*)(la + R * ARB + 16 * ((2 * g + 1) ^ aswz(R)))
                                : *(const i32x4*)(la + R * LROW + 32 * g + 16);
         const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        float asr[4];
+        // FP8 block scales: the products (row scale x weight block scale) of this chunk.  A
+        // wave's tiles lie in one 128-row weight block, except that stage 1 with separated
+        // gate and up rows has one block for its gate tiles [0, NT/2) and one for its up
+        // tiles (16-row tiles in runs of 32 rows from a multiple of 32 never straddle a
+        // block), so 4 or 8 products serve the m-tile's NT tiles.
+        float sg[4], su[4];
         if constexpr (WF == kWFp8Block) {
+          const bool two = STAGE == 1 && !(EPI && p.interleaved);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) asr[rr] = lds_as[buf][m * 16 + 4 * g + rr];
+          for (int rr = 0; rr < 4; ++rr) {
+            const float asr = lds_as[buf][m * 16 + 4 * g + rr];
+            sg[rr] = asr * wr.sb[0];
+            su[rr] = two ? asr * wr.sb[NT / 2] : sg[rr];
+          }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
             const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 a8, b8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[m][t][rr] += part[rr] * (asr[rr] * wr.sb[t]);
+            for (int rr = 0; rr < 4; ++rr) acc[m][t][rr] += part[rr] * (t < NT / 2 ? sg[rr] : su[rr]);
           } else {
             acc[m][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[m][t], 0, 0, 0, 127, 0, 127);
           }
