@@ -5,7 +5,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import B, DEV, bf16_dev, bf16_host, check_output, check_rounding, combine_f32, orc, say, synth, to_dev
+from gpu_common import (B, DEV, bf16_dev, bf16_host, check_output, check_rounding, combine_f32, h_by_slot, orc, say,
+                        synth, to_dev)
+from test_gpu_forward import check_end_to_end
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +57,11 @@ def run_share(w, data, ids_dev, wts_dev, mine, bm, tiled, n_valid=None):
     args = B.forward_args(x, w1, w1s, w2, w2s, loc, wts_dev, srt, w.wfmt, w.afmt, bm, E_loc, w.I, out, ws, a1c, a1s,
                           weight_layout=layout)
     L = B.moe_workspace_layout(args)
+    cap = B.moe_sort_capacity(w.T, w.K, E_loc, bm)
     res = dict(out=bf16_host(out), ids=loc.cpu().numpy(), weights=wts_dev.cpu().numpy(),
-               ybuf_dev=ws[L["ybuf_off"]:L["ybuf_off"] + L["ybuf_bytes"]].view(torch.float32).view(-1, w.H))
+               ybuf_dev=ws[L["ybuf_off"]:L["ybuf_off"] + L["ybuf_bytes"]].view(torch.float32).view(-1, w.H),
+               sort={k: v.cpu().numpy() for k, v in srt.items()},
+               h_sorted=ws[L["h_off"]:L["h_off"] + L["h_bytes"]].cpu().numpy().view(np.uint16).reshape(cap, w.I))
     Lo = orc.Layer(w.H, w.I, E_loc, w.K, w.wfmt, w.afmt, wl["w1"], wl["w1_scale"], wl["w2"], wl["w2_scale"])
     return res, Lo
 
@@ -90,8 +95,11 @@ def test_ep_shares(name, bm, tiled):
         check_rounding(res["out"], acc, f"ep {name} share {s_i}")
         if w.afmt == synth.A_BF16:
             check_output(acc, ref, f"ep {name} share {s_i}")
-        else:  # end-to-end with quantised activations: see full_check in test_gpu_forward
-            check_output(acc, ref, f"ep {name} share {s_i}", max_rel=0.1, row_l2=2e-2)
+        else:  # quantised activations: the staged check of full_check in test_gpu_forward
+            h_gpu = h_by_slot(res, w.T, w.K, w.I)
+            out2 = orc.stage2(Lo, h_gpu, ref_loc, res["weights"])
+            check_output(acc, out2, f"ep {name} share {s_i} stage 2 on GPU h")
+            check_end_to_end(acc, ref, out2, f"ep {name} share {s_i} end-to-end")
         no_local = (ref_loc < 0).all(axis=1)
         assert np.all(res["out"][no_local] == 0)
 

@@ -16,7 +16,9 @@ e4m3, up to 1/2 for e2m1).  The gate is staged: stage-1 h within one ulp of the
 oracle's, the GPU's a2 codes bit-exactly equal to the oracle quantiser applied to the
 GPU's own h, and the output bound against the oracle's stage 2 fed the GPU's h.  The
 end-to-end result (oracle h, oracle a2) is reported with the count of differing a2 codes
-(asserted below 0.2%) under a per-row L2 of 2e-2 and max 0.1 * rms: measured on the
+(asserted below 0.2%), and its difference from the oracle is asserted to be at most the
+difference between the oracle's outputs from its own h and from the GPU's h, plus the
+output bound (per element and per row).  Measured on the
 full-size fp8-block workload (N(0, 1/K) weights quantised per 128x128 block), the FP8
 MFMA's 128-product sums leave 2.1% of h values one ulp from the oracle's fp64 result
 (bf16 MFMA paths: 0.1-0.2%), 0.17% of a2 codes then differ, and one such step in the
@@ -27,8 +29,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import (B, DEV, bf16_dev, check_output, check_rounding, combine_f32, dev_weights, h_by_slot,
-                        layer_for, orc, run_layer, say, synth, targeted_tokens, tiled_reference, to_dev)
+from gpu_common import (B, DEV, MAX_ABS_REL_RMS, ROW_REL_L2, bf16_dev, check_output, check_rounding, combine_f32,
+                        dev_weights, h_by_slot, layer_for, orc, run_layer, say, synth, targeted_tokens,
+                        tiled_reference, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +79,9 @@ def full_check(w, data, res, tokens=None, what="", act=None):
     bf16 activations: the end-to-end output meets the output bound.
     Quantised activations: a2 codes are bit-exact given the GPU's h, the output meets
     the bound against the oracle's stage 2 fed the GPU's h, and the end-to-end result
-    (where a2 codes may differ because h was rounded differently) is reported with
-    the number of a2 codes that differ, which must stay a small fraction."""
+    (where a2 codes may differ because h was rounded differently) differs from the
+    oracle's by no more than the oracle's own outputs from the two h differ, plus the
+    bound; the number of a2 codes that differ must stay a small fraction."""
     L = layer_for(w, data, act)
     ids, wts = res["ids"], res["weights"]
     ref_ids, ref_w = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
@@ -102,10 +106,29 @@ def full_check(w, data, res, tokens=None, what="", act=None):
     c_gpu, _ = orc.quant_act(h_gpu[valid], w.afmt)
     flips = int(np.count_nonzero(c_ref != c_gpu))
     assert flips <= max(4, c_ref.size // 500), f"{what}: {flips} a2 code bytes differ"
-    # each differing a2 code moves its row by one code step (module notes): the strict bound
-    # is the stage-2 check above
-    return check_output(acc, ref, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)",
-                        max_rel=0.1, row_l2=2e-2)
+    # each differing a2 code moves its row by one code step (module notes).  End to end, the
+    # GPU may differ from the oracle by what those steps move, which the oracle computes
+    # itself (its stage 2 fed the GPU's h), plus the output bound
+    return check_end_to_end(acc, ref, out2, f"{what} end-to-end ({flips} of {c_ref.size} a2 code bytes differ)")
+
+
+def check_end_to_end(got, ref, ref_gpu_h, what):
+    """|got - ref| <= |ref_gpu_h - ref| + 2e-2 * rms(ref) per element, and per row
+    |got - ref| <= |ref_gpu_h - ref| + 1e-2 |ref| in L2: the end-to-end difference is the
+    one the oracle itself shows between its own h and the GPU's h, within the output
+    bound.  Reports the plain end-to-end figures too."""
+    got = got.astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    d, dq = np.abs(got - ref), np.abs(ref_gpu_h - ref)
+    rn = np.linalg.norm(ref, axis=1)
+    en, eq = np.linalg.norm(got - ref, axis=1), np.linalg.norm(ref_gpu_h - ref, axis=1)
+    rows = en / np.maximum(rn, 1e-300)
+    say(f"{what}: max|d|/rms={d.max() / rms:.3e} worst row rel L2={rows.max():.3e} "
+        f"(the oracle's own, from the GPU's h: {dq.max() / rms:.3e}, {(eq / np.maximum(rn, 1e-300)).max():.3e})")
+    excess = d - dq - MAX_ABS_REL_RMS * rms
+    assert excess.max() <= 0, f"{what}: end-to-end error exceeds the a2-step difference + bound at {np.argwhere(excess > 0)[:5]}"
+    rex = en - eq - ROW_REL_L2 * rn
+    assert rex.max() <= 0, f"{what}: row L2 exceeds the a2-step difference + bound in rows {np.argwhere(rex > 0)[:5]}"
 
 
 SMALL = []
@@ -129,6 +152,18 @@ def test_small_all_formats(fmt, bm, tiled):
     data = synth.make_all(w)
     res = run_layer(w, data, block_m=bm, tiled=tiled)
     full_check(w, data, res, what=f"{w.name}/bm{bm}/{'tiled' if tiled else 'canon'}")
+
+
+@pytest.mark.parametrize("fmt", [W4A16, W4A4, FP8B, FP8C], ids=["w4a16", "w4a4", "fp8b", "fp8c"])
+def test_lds_ring_wraps(fmt):
+    # 128-row blocks on tiled weights: more K chunks than the LDS ring holds (H=1440 is
+    # 11.25 chunks, I=1056 8.25), so every ring buffer is reused, with ragged K tails, two
+    # row blocks per expert (the second partly padding) and ragged column strips
+    w = small(fmt, T=300, H=1440, I=1056, E=4, k=2, seed=71)
+    say(f"ring wrap {w.name} bm=128 tiled T={w.T} H={w.H} I={w.I} E={w.E_total} K={w.K}")
+    data = synth.make_all(w)
+    res = run_layer(w, data, block_m=128, tiled=True)
+    full_check(w, data, res, what=f"{w.name}/ring-wrap")
 
 
 @pytest.mark.parametrize("wfmt,N,K", [(synth.W_MXFP4, 64, 320), (synth.W_MXFP4, 576, 2880),
