@@ -1593,16 +1593,8 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : (WF == kWBf16 ? 2 : 4);
   if constexpr (kSplit) {
-    // Stage 2 with few row blocks (one or two tokens): narrower strips, so that the
-    // grid still covers every CU, down to one tile per wave
-    const long target = 256L * MOE_KSPLIT_WGS_PER_CU;
-    if constexpr (STAGE == 2 && NT >= 4) {
-      if ((long)p_in.num_blocks * ((p_in.N + 16 * NT - 1) / (16 * NT)) < target) {
-        if ((long)p_in.num_blocks * ((p_in.N + 32 - 1) / 32) >= target)
-          return launch_ksplit<STAGE, WF, AF, BM, 2, WL, EPI>(p_in, stream);
-        return launch_ksplit<STAGE, WF, AF, BM, 1, WL, EPI>(p_in, stream);
-      }
-    }
+    // (one or two tokens leave CUs idle here, e.g. 128 workgroups for stage 2 of a 4096-wide
+    // layer; strips of 2 or 1 tiles per wave that fill the chip measured 1-3% slower)
     return launch_ksplit<STAGE, WF, AF, BM, NT, WL, EPI>(p_in, stream);
   } else {
   constexpr int COLS_PER_WG = (STAGE == 1) ? 32 * NT : 64 * NT;
