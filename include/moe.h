@@ -374,8 +374,11 @@ moe_status moe_tile_weights(moe_wfmt wfmt, int E, int N, int K, const uint8_t* w
 moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I);
 
 /* A row tile for moe_align_sort / moe_experts_forward suited to T*K slots over E_total
- * experts (host-side heuristic; any value in {16, 32, 64, 128} is valid). */
-int moe_pick_block_m(int T, int K, int E_total);
+ * experts, weight format wfmt and weight layout (host-side heuristic; any value in
+ * {16, 32, 64, 128} is valid): 16 or 32 rows for few rows per expert, else 64, except
+ * 128 for FP8 128x128-block weights in the tiled layout with at least 96 rows per expert
+ * on average, where the LDS-staged 128-row kernel is the faster one. */
+int moe_pick_block_m(int T, int K, int E_total, moe_wfmt wfmt, moe_weight_layout layout);
 
 /* Profiling hook.  While enabled (count == 4), moe_experts_forward calls made on this
  * thread record, on their stream, events[0] just before the stage-1 GEMM, events[1] just

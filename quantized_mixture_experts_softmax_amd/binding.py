@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
         L.moe_supports.restype = S
         L.moe_supports.argtypes = [I, I, I, I, I]
         L.moe_pick_block_m.restype = I
-        L.moe_pick_block_m.argtypes = [I, I, I]
+        L.moe_pick_block_m.argtypes = [I, I, I, I, I]
         L.moe_profile_events.restype = S
         L.moe_profile_events.argtypes = [P, I]
         L.moe_tiled_weight_bytes.restype = ctypes.c_size_t
@@ -174,8 +174,8 @@ def moe_supports(wfmt: int, afmt: int, H: int, I: int, act: int = ACT_SILU) -> b
     return lib().moe_supports(wfmt, afmt, act, H, I) == MOE_OK
 
 
-def moe_pick_block_m(T: int, K: int, E_total: int) -> int:
-    return lib().moe_pick_block_m(T, K, E_total)
+def moe_pick_block_m(T: int, K: int, E_total: int, wfmt: int = W_MXFP4, layout: int = LAYOUT_CANONICAL) -> int:
+    return lib().moe_pick_block_m(T, K, E_total, wfmt, layout)
 
 
 def moe_sort_capacity(T: int, K: int, E_total: int, block_m: int) -> int:
@@ -478,7 +478,7 @@ class MoELayer:
     def _buffers(self, T: int, dev):
         key = (T, str(dev))
         if key not in self._bufs:
-            bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total)
+            bm = self.block_m or moe_pick_block_m(T, self.K, self.E_total, self.wfmt, self.weight_layout)
             if self.wfmt == W_BF16 and (bm == 32 or (bm == 16 and max(self.H, self.I) > BF16_SMALL_BLOCK_MAX_K)):
                 bm = 64  # bf16 weights: no 32-row kernel; 16-row blocks only with the activation tile in LDS
             cap = moe_sort_capacity(T, self.K, self.E_local, bm)

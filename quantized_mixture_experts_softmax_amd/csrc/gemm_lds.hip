@@ -377,16 +377,24 @@ __global__ __launch_bounds__(128 * WN, 1) void moe_gemm_lds_kernel(const GemmPar
         const i32x4 hi = *(const i32x4*)(la + R * ARB + 16 * ((2 * g + 1) ^ AT::swz(R)));
         const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if constexpr (AF == kAFp8G128) {
+          // row scale x weight block scale, one product per row and block: a column
+          // group's tiles lie in one 128-row weight block, except that stage 1 has one for
+          // its gate tiles (t < 2) and one for its up tiles (runs of 32 rows from a
+          // multiple of 32 never straddle a block)
           const float* las = (const float*)(st + LS::kAs);
-          float asr[4];
+          float sg[4], su[4];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) asr[rr] = las[64 * wm + 16 * m + 4 * g + rr];
+          for (int rr = 0; rr < 4; ++rr) {
+            const float asr = las[64 * wm + 16 * m + 4 * g + rr];
+            sg[rr] = asr * sb[0];
+            su[rr] = STAGE == 1 ? asr * sb[2] : sg[rr];
+          }
 #pragma unroll
           for (int t = 0; t < kNT; ++t) {
             const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 a8, b8[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[m][t][rr] += part[rr] * (asr[rr] * sb[t]);
+            for (int rr = 0; rr < 4; ++rr) acc[m][t][rr] += part[rr] * (t < 2 ? sg[rr] : su[rr]);
           }
         } else {
 #pragma unroll

@@ -34,7 +34,7 @@ int main() {
   CHECK(moe_supports(MOE_W_MXFP4, MOE_A_FP8_G128, MOE_ACT_SILU, 2880, 2880) == MOE_EUNSUPPORTED);
   CHECK(moe_supports(MOE_W_FP8_BLOCK128, MOE_A_FP8_G128, MOE_ACT_SILU, 100, 2880) == MOE_EINVAL);
   for (int T = 0; T < 9000; T += 997) {
-    const int bm = moe_pick_block_m(T, 4, 128);
+    const int bm = moe_pick_block_m(T, 4, 128, MOE_W_FP8_BLOCK128, MOE_LAYOUT_TILED);
     CHECK(bm == 16 || bm == 32 || bm == 64 || bm == 128);
   }
   CHECK(moe_tile_weights(MOE_W_MXFP4, 2, 60, 256, nullptr, nullptr, nullptr, nullptr) == MOE_EINVAL);

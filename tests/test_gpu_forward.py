@@ -329,7 +329,7 @@ def test_full_size_prefill_w4a4():
     w = synth.WORKLOADS["prefill-w4a4"]
     say(f"full-size {w.name}: T={w.T}")
     data = synth.make_all(w)
-    res = run_layer(w, data)
+    res = run_layer(w, data, tiled=True)  # the benchmark's launch configuration (tiled, picked block_m)
     # a1 codes are an integer product of the GPU quantiser: bit-exact on every token
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
@@ -340,7 +340,8 @@ def test_full_size_fp8_block_shared():
     w = synth.WORKLOADS["fp8-block"]
     say(f"full-size {w.name}: T={w.T} H={w.H} I={w.I} E={w.E}+{w.n_shared}")
     data = synth.make_all(w)
-    res = run_layer(w, data)
+    res = run_layer(w, data, tiled=True)  # the benchmark's launch configuration (tiled, picked block_m)
+    say(f"{w.name}: block_m {res['bm']}")
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
     assert np.all(res["ids"][:, w.topk] == w.E) and np.all(res["weights"][:, w.topk] == 1.0)
@@ -361,7 +362,7 @@ def test_full_size_fp8_channel_sweep(fp8_channel_data, T):
     w = w0.with_T(T)
     say(f"full-size {w.name}: T={T}")
     data = dict(d0, x=np.ascontiguousarray(d0["x"][:T]), logits=np.ascontiguousarray(d0["logits"][:T]))
-    res = run_layer(w, data)
+    res = run_layer(w, data, tiled=True)  # the benchmark's launch configuration (tiled, picked block_m)
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
     full_check(w, data, res, tokens=targeted_tokens(res, T, w.K, n_min=16, seed=8), what=f"{w.name}/T{T}")
