@@ -215,11 +215,17 @@ hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int fmt, cons
   } else if (fmt == kAFp8Token) {
     // one workgroup per row; the smallest of these shapes that holds the row, so that a
     // thread has several 16-byte loads in flight: 256 threads x 1..8 octets (up to 16384
-    // columns), then 512 and 1024 threads x 8 octets (up to 65536)
+    // columns), then 512 and 1024 threads x 8 octets (up to 65536).  With few rows (up to
+    // 512, e.g. a2 of one to a few tokens) the chip is mostly idle and each row's latency
+    // counts: 1024 threads per wide row, so that a thread encodes fewer values in sequence.
     const int oct = cols / 8;
     float* sc = (float*)scales;
     const unsigned R = (unsigned)rows;
-    if (oct <= 256) quant_fp8_token_kernel<256, 1><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    if (rows <= 512 && oct > 512) {
+      if (oct <= 2048) quant_fp8_token_kernel<1024, 2><<<R, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+      else if (oct <= 4096) quant_fp8_token_kernel<1024, 4><<<R, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+      else quant_fp8_token_kernel<1024, 8><<<R, 1024, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
+    } else if (oct <= 256) quant_fp8_token_kernel<256, 1><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
     else if (oct <= 512) quant_fp8_token_kernel<256, 2><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
     else if (oct <= 1024) quant_fp8_token_kernel<256, 4><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);
     else if (oct <= 2048) quant_fp8_token_kernel<256, 8><<<R, 256, 0, stream>>>(x, rows, cols, rows_dev, codes, sc);

@@ -159,6 +159,9 @@ QUANT_CASES = [("fp8-g128", B.A_FP8_G128, 40, 7168), ("fp8-g128-ragged", B.A_FP8
                ("fp8-token-2048", B.A_FP8_TOKEN, 4, 2048), ("fp8-token-2080", B.A_FP8_TOKEN, 4, 2080),
                ("fp8-token-16416", B.A_FP8_TOKEN, 2, 16416), ("fp8-token-32768", B.A_FP8_TOKEN, 2, 32768),
                ("fp8-token-max", B.A_FP8_TOKEN, 3, 65536),
+               # many rows: the 256- and 512-thread shapes (few rows take 1024 threads per row)
+               ("fp8-token-rows-8192", B.A_FP8_TOKEN, 600, 8192), ("fp8-token-rows-14336", B.A_FP8_TOKEN, 600, 14336), ("fp8-token-rows-32768", B.A_FP8_TOKEN, 520, 32768),
+               ("fp8-token-rows-65536", B.A_FP8_TOKEN, 513, 65536),
                # the group quantisers take 4 runs of lanes per workgroup: a grid whose last
                # workgroup is partly past the end
                ("fp8-g128-runs", B.A_FP8_G128, 65, 384), ("mxfp4-runs", B.A_MXFP4_G32, 37, 224)]
