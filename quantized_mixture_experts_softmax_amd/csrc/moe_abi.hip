@@ -156,13 +156,17 @@ moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I)
 
 int moe_pick_block_m(int T, int K, int E_total, moe_wfmt wfmt, moe_weight_layout layout) {
   if (E_total <= 0) return 16;
+  // Measured on MI355X (bench steps, every format): 16-row blocks win up to ~16 rows per
+  // expert (the persistent kernel, with the route fused in), except for FP8 block weights
+  // with more than one row per expert (T = 32 .. 256 over 257 experts: 64 rows 12-22%
+  // faster); above that 64-row blocks win everywhere, 32-row blocks never (1.1-2.6x slower
+  // than 64 at 20-36 rows per expert).
   const double rows = (double)T * K / E_total;
-  if (rows <= 16) return 16;
-  if (rows <= 48) return 32;
+  if (rows <= 16 && !(wfmt == MOE_W_FP8_BLOCK128 && rows > 1)) return 16;
   // FP8 block weights, tiled: the 128-row LDS-staged kernel (4.13 against 4.30 ms per step
-  // at T = 4096, 257 experts, top-8 + 1 shared, on MI355X)
+  // at T = 4096, 257 experts, top-8 + 1 shared)
   if (wfmt == MOE_W_FP8_BLOCK128 && layout == MOE_LAYOUT_TILED && rows >= 96) return 128;
-  return 64;  // other large batches: 64-row blocks keep two waves per SIMD resident (measured faster than 128)
+  return 64;  // 64-row blocks keep two waves per SIMD resident (measured faster than 128)
 }
 
 moe_status moe_route_topk(const float* router_logits, int T, int E, int topk, moe_score score, int renormalize,

@@ -162,7 +162,12 @@ def test_pick_block_m(lib):
     assert B.moe_pick_block_m(4096, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 128
     assert B.moe_pick_block_m(4096, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_CANONICAL) == 64
     assert B.moe_pick_block_m(4096, 9, 257, B.W_MXFP4, B.LAYOUT_TILED) == 64
-    assert B.moe_pick_block_m(1024, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 32
+    assert B.moe_pick_block_m(1024, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 64
+    # 17..95 rows per expert: 64-row blocks (32-row blocks measured slower everywhere)
+    assert B.moe_pick_block_m(1024, 4, 128) == 64 and B.moe_pick_block_m(128, 2, 8) == 64
+    # FP8 block weights: 64-row blocks above one row per expert, 16 below
+    assert B.moe_pick_block_m(64, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 64
+    assert B.moe_pick_block_m(16, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 16
 
 
 def test_tiled_weight_bytes_and_validation(lib):
