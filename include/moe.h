@@ -377,7 +377,7 @@ moe_status moe_supports(moe_wfmt wfmt, moe_afmt afmt, moe_act act, int H, int I)
  * experts, weight format wfmt and weight layout (host-side heuristic; any value in
  * {16, 32, 64, 128} is valid): 16 rows for up to 16 rows per expert on average (FP8
  * 128x128-block weights: up to 1), else 64, except 128 for FP8 block weights in the
- * tiled layout with at least 96 rows per expert, where the LDS-staged 128-row kernel is
+ * tiled layout with at least 64 rows per expert, where the LDS-staged 128-row kernel is
  * the faster one.  32-row blocks are never picked (measured slower than 64). */
 int moe_pick_block_m(int T, int K, int E_total, moe_wfmt wfmt, moe_weight_layout layout);
 

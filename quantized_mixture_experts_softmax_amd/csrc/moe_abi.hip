@@ -164,8 +164,8 @@ int moe_pick_block_m(int T, int K, int E_total, moe_wfmt wfmt, moe_weight_layout
   const double rows = (double)T * K / E_total;
   if (rows <= 16 && !(wfmt == MOE_W_FP8_BLOCK128 && rows > 1)) return 16;
   // FP8 block weights, tiled: the 128-row LDS-staged kernel (4.13 against 4.30 ms per step
-  // at T = 4096, 257 experts, top-8 + 1 shared)
-  if (wfmt == MOE_W_FP8_BLOCK128 && layout == MOE_LAYOUT_TILED && rows >= 96) return 128;
+  // at T = 4096, 257 experts, top-8 + 1 shared; 2.85 against 2.91 at T = 2048)
+  if (wfmt == MOE_W_FP8_BLOCK128 && layout == MOE_LAYOUT_TILED && rows >= 64) return 128;
   return 64;  // 64-row blocks keep two waves per SIMD resident (measured faster than 128)
 }
 
