@@ -158,8 +158,9 @@ def test_pick_block_m(lib):
     assert B.moe_pick_block_m(64, 4, 32) == 16
     assert B.moe_pick_block_m(8192, 4, 128) == 64  # 128-row blocks run one wave per SIMD
     assert B.moe_pick_block_m(256, 2, 8) == 64
-    # FP8 128x128-block weights, tiled, >= 96 rows per expert: the 128-row LDS-staged kernel
+    # FP8 128x128-block weights, tiled, >= 64 rows per expert: the 128-row LDS-staged kernel
     assert B.moe_pick_block_m(4096, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 128
+    assert B.moe_pick_block_m(2048, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 128
     assert B.moe_pick_block_m(4096, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_CANONICAL) == 64
     assert B.moe_pick_block_m(4096, 9, 257, B.W_MXFP4, B.LAYOUT_TILED) == 64
     assert B.moe_pick_block_m(1024, 9, 257, B.W_FP8_BLOCK128, B.LAYOUT_TILED) == 64
