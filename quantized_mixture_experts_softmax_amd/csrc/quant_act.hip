@@ -5,9 +5,10 @@
 //
 // The encoders take their decisions in IEEE fp32 exactly as documented for
 // moe_quant_act: amax is exact, s = amax / 448 and x / s are correctly rounded fp32
-// divisions (hipcc keeps fp32 division correctly rounded unless fast-math is asked
-// for), and the element rounding is done in integer-exact steps, so the codes are
-// bit-identical to the oracle's given the same bf16 input.
+// divisions (s by hipcc's division, which stays correctly rounded unless fast-math is
+// asked for; x / s by a one-FMA correction of x * (1/s), see div_rn), and the element
+// rounding is done in integer-exact steps, so the codes are bit-identical to the oracle's
+// given the same bf16 input.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -31,13 +32,37 @@ __device__ __forceinline__ float amax8(const float (&f)[8]) {
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
   return m;
 }
+// x / s, correctly rounded, by Markstein's method (P. Markstein, IBM J. Res. Dev. 34(1),
+// 1990): with r = RN(1/s), q = RN(x r) lies within an ulp of x / s, the remainder
+// x - s q is exact in one FMA, and RN(q + (x - s q) r) is the correctly rounded quotient
+// unless the remainder underflows.  For bf16 x with |x| <= 448 s and s >= 2^-80 (smaller
+// scales take the plain division) an exhaustive host check over every such pair finds the
+// result equal to the correctly rounded division wherever the quotient is at least 2^-11;
+// smaller quotients, where underflow can cost the last bit, all encode to a zero code.
+// (The result takes the sign of x: for x = -0 the FMAs would return +0, while -0 / s is -0
+// and encodes to the code 0x80.)
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q = x * r;
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q, s, x), r, q), x);
+}
+constexpr float kMinFastScale = 0x1.0p-80f;  // smaller scales take the plain division
+
 // e4m3 codes of f[i] / s, packed little-endian into 8 bytes
 __device__ __forceinline__ uint2 e4m3_pack8(const float (&f)[8], float s) {
   uint32_t lo = 0, hi = 0;
+  if (s >= kMinFastScale) {
+    const float r = 1.0f / s;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_encode(f[i] / s) << (8 * i);
-    hi |= e4m3_encode(f[4 + i] / s) << (8 * i);
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_encode(div_rn(f[i], s, r)) << (8 * i);
+      hi |= e4m3_encode(div_rn(f[4 + i], s, r)) << (8 * i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_encode(f[i] / s) << (8 * i);
+      hi |= e4m3_encode(f[4 + i] / s) << (8 * i);
+    }
   }
   return make_uint2(lo, hi);
 }
