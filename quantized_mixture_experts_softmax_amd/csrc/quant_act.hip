@@ -47,16 +47,25 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
 }
 constexpr float kMinFastScale = 0x1.0p-80f;  // smaller scales take the plain division
 
+// Four e4m3 codes of v[0..3] packed little-endian, by the hardware conversion
+// (v_cvt_pk_fp8_f32: round to nearest even, OCP e4m3fn).  Checked on MI355X against
+// e4m3_encode over every finite fp32 value: identical for |v| < 448, and v in [448, 500]
+// also gives 0x7E; the quotients here are at most RN(448 (1 + 2^-24)).
+__device__ __forceinline__ uint32_t e4m3_hw4(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
+}
+
 // e4m3 codes of f[i] / s, packed little-endian into 8 bytes
 __device__ __forceinline__ uint2 e4m3_pack8(const float (&f)[8], float s) {
   uint32_t lo = 0, hi = 0;
   if (s >= kMinFastScale) {
     const float r = 1.0f / s;
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_encode(div_rn(f[i], s, r)) << (8 * i);
-      hi |= e4m3_encode(div_rn(f[4 + i], s, r)) << (8 * i);
-    }
+    for (int i = 0; i < 8; ++i) q[i] = div_rn(f[i], s, r);
+    lo = e4m3_hw4(q[0], q[1], q[2], q[3]);
+    hi = e4m3_hw4(q[4], q[5], q[6], q[7]);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -165,10 +174,15 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     const int es = mx_shared_exp(m);
     const float inv = exp2i(-es);
     if (live[u]) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        packed |= (e2m1_encode(f[u][2 * i] * inv) | (e2m1_encode(f[u][2 * i + 1] * inv) << 4)) << (8 * i);
+      // e2m1 codes of x 2^-es (an exact product) by the hardware conversion at unit scale
+      // (v_cvt_scalef32_pk_fp4_f32: round to nearest even, saturating at 6), checked on
+      // MI355X against e2m1_encode over every finite fp32 value: identical; byte i holds
+      // elements 2i (low nibble) and 2i + 1
+      const float(&g)[8] = f[u];
+      uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, g[0] * inv, g[1] * inv, 1.0f, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, g[2] * inv, g[3] * inv, 1.0f, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, g[4] * inv, g[5] * inv, 1.0f, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, g[6] * inv, g[7] * inv, 1.0f, 3);
       *(uint32_t*)(codes + (size_t)r[u] * (cols / 2) + c[u] / 2) = packed;
       if ((c[u] & 31) == 0) scales[(size_t)r[u] * (cols / 32) + c[u] / 32] = (uint8_t)(es + 127);
     }
