@@ -112,7 +112,10 @@ struct WLayout {
 // the hot path); 1 = activation, row order and biases as GemmParams says.
 template <int EPI>
 __device__ __forceinline__ float glu(const GemmParams& p, float g, float u) {
-  if constexpr (EPI == 0) return g / (1.0f + __expf(-g)) * u;
+  // SiLU as g * rcp(1 + e^-g): the hardware reciprocal (within an ulp) in place of the
+  // correctly rounded division; h is rounded to bf16 next, so this moves h by at most one
+  // bf16 ulp in the rare values that sit on a rounding boundary (g -> -inf: rcp(inf) = 0)
+  if constexpr (EPI == 0) return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
   else return glu_act(p, g, u);
 }
 
