@@ -328,8 +328,8 @@ def main() -> int:
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--extra", choices=["all", "none"], default="all",
                     help="all: also time the prefill-sized workloads and the fp8-channel sweep (extra_configs)")
-    ap.add_argument("--extra-steps", type=int, default=10)
-    ap.add_argument("--extra-warmup", type=int, default=3)
+    ap.add_argument("--extra-steps", type=int, default=30)
+    ap.add_argument("--extra-warmup", type=int, default=5)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
