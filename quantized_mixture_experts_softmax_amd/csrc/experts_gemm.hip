@@ -897,11 +897,29 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
   };
 
   clear();
-  // One item in flight ahead of the MFMAs.  Each half-iteration issues the next
-  // item's loads, then computes the previous one; sched_barrier keeps the scheduler
-  // from sinking a prefetch below the MFMAs that follow it.
   WeightRegs<WF, NT> w0, w1;
   ARegs<AF, MT> a0, a1;
+  if (n_str == 1) {
+    // One strip (the usual case for one to a few tokens): the same stream with the strip's
+    // epilogue after the loop.  With the epilogue inside the loop, as below, the compiler
+    // drains every load in flight where the epilogue's branch rejoins the stream.
+    load(0, w0, a0);
+    for (int i = 0; i < n_items; i += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(i + 1, w1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(i + 2, w0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < n_items) compute(w1, a1);
+    }
+    finish_strip(0);
+    return;
+  }
+  // Several strips: one item in flight ahead of the MFMAs.  Each half-iteration issues the
+  // next item's loads, then computes the previous one; sched_barrier keeps the scheduler
+  // from sinking a prefetch below the MFMAs that follow it.
   load(0, w0, a0);
   for (int i = 0; i < n_items; i += 2) {
     __builtin_amdgcn_sched_barrier(0);
