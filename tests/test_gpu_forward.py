@@ -81,7 +81,8 @@ def full_check(w, data, res, tokens=None, what="", act=None):
     the bound against the oracle's stage 2 fed the GPU's h, and the end-to-end result
     (where a2 codes may differ because h was rounded differently) differs from the
     oracle's by no more than the oracle's own outputs from the two h differ, plus the
-    bound; the number of a2 codes that differ must stay a small fraction."""
+    bound; the number of a2 codes that differ must stay a small fraction.
+    Returns the plain end-to-end figures (max |d| / rms, worst row relative L2)."""
     L = layer_for(w, data, act)
     ids, wts = res["ids"], res["weights"]
     ref_ids, ref_w = orc.route_topk(data["logits"], w.topk, w.score, True, w.n_shared, w.shared_weight)
@@ -129,6 +130,7 @@ def check_end_to_end(got, ref, ref_gpu_h, what):
     assert excess.max() <= 0, f"{what}: end-to-end error exceeds the a2-step difference + bound at {np.argwhere(excess > 0)[:5]}"
     rex = en - eq - ROW_REL_L2 * rn
     assert rex.max() <= 0, f"{what}: row L2 exceeds the a2-step difference + bound in rows {np.argwhere(rex > 0)[:5]}"
+    return d.max() / rms, rows.max()
 
 
 SMALL = []
@@ -365,7 +367,13 @@ def test_full_size_fp8_channel_sweep(fp8_channel_data, T):
     res = run_layer(w, data, tiled=True)  # the benchmark's launch configuration (tiled, picked block_m)
     rc, rs = orc.quant_act(data["x"], w.afmt)
     assert np.array_equal(res["a1_codes"], rc) and np.array_equal(res["a1_scales"], rs)
-    full_check(w, data, res, tokens=targeted_tokens(res, T, w.K, n_min=16, seed=8), what=f"{w.name}/T{T}")
+    e_max, e_row = full_check(w, data, res, tokens=targeted_tokens(res, T, w.K, n_min=16, seed=8),
+                              what=f"{w.name}/T{T}")
+    # per-token a2 over I = 14336 values and two softmax-weighted slots: one a2 code step
+    # moves an output row by about 1/8 of one of 14336 terms, so the output bound holds end
+    # to end here as well, and is asserted as it stands
+    assert e_max <= MAX_ABS_REL_RMS, f"{w.name}/T{T}: end-to-end max|d| = {e_max:.3e} rms"
+    assert e_row <= ROW_REL_L2, f"{w.name}/T{T}: end-to-end row L2 = {e_row:.3e}"
 
 
 FP8T = (synth.W_FP8_TENSOR, synth.A_FP8_TENSOR)
