@@ -136,6 +136,30 @@ def test_align_sort(T, K, E, bm):
     assert int(got["num_padded"].cpu()[0]) == ref["num_padded"]
 
 
+@pytest.mark.parametrize("T,K,E,bm,offset", [(16384, 4, 128, 64, 0), (20000, 4, 61, 32, 1), (20000, 4, 61, 32, 0),
+                                              (3000, 3, 9, 16, 3)])
+def test_align_sort_id_layouts(T, K, E, bm, offset):
+    """ids as a view into a larger buffer (starting 4 or 12 bytes past an aligned
+    address) and at 16 workgroup chunks exactly, with ids outside [0, E) mixed in."""
+    say(f"align_sort layouts T={T} K={K} E={E} bm={bm} offset={offset}")
+    rng = np.random.default_rng(T + K + E + bm + offset)
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    ids[rng.random((T, K)) < 0.01] = -1
+    ids[rng.random((T, K)) < 0.01] = E + 3
+    buf = torch.empty(offset + T * K, dtype=torch.int32, device=DEV)
+    buf[offset:] = to_dev(ids).reshape(-1)
+    view = buf[offset:].view(T, K)
+    assert (view.data_ptr() % 16) == 4 * offset % 16
+    got = B.moe_align_sort(view, E, bm)
+    torch.cuda.synchronize()
+    ref = orc.align_sort(ids, E, bm)
+    for key in ("expert_counts", "expert_offsets", "sorted_slots"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    nb = len(ref["block_expert"])
+    assert np.array_equal(got["block_expert"].cpu().numpy()[:nb], ref["block_expert"])
+    assert int(got["num_padded"].cpu()[0]) == ref["num_padded"]
+
+
 def test_align_sort_invalid_ids_dropped():
     ids = np.array([[0, 5], [9, -1], [2, 2], [5, 5]], np.int32)
     got = B.moe_align_sort(to_dev(ids), 6, 16)
