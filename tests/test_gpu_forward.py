@@ -168,6 +168,30 @@ def test_lds_ring_wraps(fmt):
     full_check(w, data, res, what=f"{w.name}/ring-wrap")
 
 
+RING64 = [(W4A16, False, False), (W4A4, True, False), (FP8B, True, False), (FP8C, True, False),
+          (FP8C, False, False), ((synth.W_FP8_TENSOR, synth.A_FP8_TENSOR), True, False),
+          ((synth.W_BF16, synth.A_BF16), False, False), (W4A16, True, True), (FP8C, True, True)]
+
+
+@pytest.mark.parametrize("fmt,tiled,oai", RING64,
+                         ids=[f"w{f[0]}a{f[1]}-{'tiled' if t else 'canon'}{'-bias-oai' if o else ''}"
+                              for f, t, o in RING64])
+def test_bm64_long_k(fmt, tiled, oai):
+    """64-row blocks over a longer stage-2 K: I = 1056 is 9 K chunks with a ragged last
+    one, more than the kernel's register ring period (6 chunks at two chunks ahead), so
+    the ring wraps in stage 2 as well as stage 1, on every format and layout, with biases
+    and SwiGLU-OAI on interleaved rows."""
+    w = small(fmt, T=40, H=320, I=1056, E=4, k=2, seed=83)
+    data = synth.make_all(w)
+    act = None
+    if oai:
+        act, data = oai_case(w, data, True, True, kind=1)
+    what = f"{w.name}/bm64-long-k/{'tiled' if tiled else 'canon'}{'/bias-oai' if oai else ''}"
+    say(f"forward {what} T={w.T} H={w.H} I={w.I}")
+    res = run_layer(w, data, block_m=64, tiled=tiled, act=act)
+    full_check(w, data, res, what=what, act=act)
+
+
 @pytest.mark.parametrize("wfmt,N,K", [(synth.W_MXFP4, 64, 320), (synth.W_MXFP4, 576, 2880),
                                       (synth.W_FP8_BLOCK128, 96, 352), (synth.W_FP8_CHANNEL, 32, 4096)])
 def test_tile_weights_layout(wfmt, N, K):
