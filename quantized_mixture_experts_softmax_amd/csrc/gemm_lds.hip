@@ -256,13 +256,11 @@ __global__ __launch_bounds__(128 * WN, 1) void moe_gemm_lds_kernel(const GemmPar
       }
     }
     if constexpr (AF == kAFp8G128) {
-      if (w < 2) {
-        const int r = w * 64 + lane;  // == tid
+      if (w < 2) {  // row tid = 64 w + lane: its fp32 scale lands at kAs + 4 tid
         const bool ok = live && s_ok;
         const MOE_GLOBAL uint8_t* src =
             ok ? (const MOE_GLOBAL uint8_t*)((const float*)p.a_scale + (size_t)s_row * nch + c) : zp;
         dma4((const void*)src, st + LS::kAs + (size_t)w * 256);
-        (void)r;
       }
     }
   };
