@@ -96,6 +96,27 @@ def test_layer_forward_decode_full_size():
     full_check(w, data, fused, what="decode fused")
 
 
+@pytest.fixture(scope="module")
+def decode_data():
+    w = synth.WORKLOADS["decode"]
+    return w, synth.make_all(w)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 63])
+def test_layer_forward_decode_token_sweep(decode_data, T):
+    """The decode layer's weights at fewer tokens (prefixes of the 64-token draw): with 1..63
+    tokens over 32 experts some experts get no rows and the workgroups' shares of the
+    (unit, K chunk) steps change; the routed stage 1 still equals the separate calls bit
+    for bit and meets the oracle bound on every token."""
+    w0, d0 = decode_data
+    w = w0.with_T(T)
+    data = dict(d0, x=np.ascontiguousarray(d0["x"][:T]), logits=np.ascontiguousarray(d0["logits"][:T]))
+    say(f"layer_forward decode T={T}")
+    fused, sep = both_paths(w, data, tiled=True)
+    assert_same(fused, sep, f"decode T={T}")
+    full_check(w, data, fused, what=f"decode T={T} fused")
+
+
 def test_layer_forward_tied_logits():
     """Router logits with many equal values (signed zeros included) on the decode-sized
     expert count: the in-kernel routing breaks ties as the separate router does."""
