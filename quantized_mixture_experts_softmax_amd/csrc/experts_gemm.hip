@@ -65,6 +65,13 @@ namespace moe {
 #endif
 // Workgroups per CU the small-block launch is sized for (strips per workgroup grow
 // until the grid is about this many workgroups per CU).
+// Column tiles per wave of the 64-row kernel for w4a4 (4 for the other formats).  Six
+// tiles cut the activation bytes per flop through the vector-memory return path, which
+// bounds w4a4 here: prefill-w4a4 (T = 8192) 1.26 against 1.33 ms per step on MI355X
+// (stage 2 -13%, stage 1 -2.5%), at ring depth 1 (depth 2 spills at six tiles).
+#ifndef MOE_NT_F4A4
+#define MOE_NT_F4A4 6
+#endif
 #ifndef MOE_KSPLIT_WGS_PER_CU
 #define MOE_KSPLIT_WGS_PER_CU 2
 #endif
@@ -200,21 +207,28 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   }
   // Tiled MXFP4 with MXFP4 activations: a lane's E8M0 byte for tile t is byte `lane` of
   // the 64-byte scale part of tile t's block.  One dword load per lane fetches the scales
-  // of all four tiles of a chunk (lane l reads bytes [4 (l % 16), +4) of tile l / 16) in
-  // place of a byte load per tile; each lane then takes its byte from lane 16 t + l / 4
-  // with ds_bpermute.  On large w4a4 batches the vector-memory return path (TD), not HBM
-  // or MFMA, bounds this kernel, and a byte load costs it about half a 16-byte one
-  // (counters on MI355X); the step gained 6%.  w4a16, whose LDS pipe carries four times
-  // the A reads, lost 9% with it and keeps the byte loads.
+  // of four tiles of a chunk (group q: lane l reads bytes [4 (l % 16), +4) of tile
+  // 4 q + l / 16) in place of a byte load per tile; each lane then takes its byte of tile
+  // t from lane 16 (t % 4) + l / 4 of group t / 4 with ds_bpermute.  On large w4a4
+  // batches the vector-memory return path (TD), not HBM or MFMA, bounds this kernel, and
+  // a byte load costs it about half a 16-byte one (counters on MI355X); the step gained
+  // 6%.  w4a16, whose LDS pipe carries four times the A reads, lost 9% with it and keeps
+  // the byte loads.
   constexpr bool kScaleDword = (WF == kWMxfp4) && (AF == kAMxfp4) && (WL != 0) && (MOE_SCALE_DWORD != 0);
-  static_assert(!kScaleDword || NT <= 4, "one dword per lane holds the scales of four tiles");
-  const uint8_t* ws4_src = nullptr;
-  if constexpr (kScaleDword) {
-    const int tt = (lane >> 4) % NT;
-    const uint8_t* b = ws_src[0];
+  constexpr int NG = (NT + 3) / 4;  // scale dwords per lane and chunk
+  static_assert(!kScaleDword || NT <= 4 * kScaleGroups, "WeightRegs holds the scale dwords of this many tiles");
+  const uint8_t* ws4_src[NG];
 #pragma unroll
-    for (int t = 1; t < NT; ++t) b = (tt == t) ? ws_src[t] : b;
-    ws4_src = b - lane + 4 * (lane & 15);
+  for (int q = 0; q < NG; ++q) {
+    ws4_src[q] = nullptr;
+    if constexpr (kScaleDword) {
+      // lanes whose tile 4 q + l / 16 does not exist read the last tile's bytes (unused)
+      const int tt = min(4 * q + (lane >> 4), NT - 1);
+      const uint8_t* b = ws_src[0];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) b = (tt == t) ? ws_src[t] : b;
+      ws4_src[q] = b - lane + 4 * (lane & 15);
+    }
   }
 
   auto load_a = [&](int c, i32x4 (&reg)[AIT]) {
@@ -260,12 +274,15 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
       }
     }
     // (the tail chunk's block holds zero scale bytes past K; chunks past the end read the zero page)
-    if constexpr (kScaleDword) r.s4 = ld_global<uint32_t>(ws4_src, (size_t)c * WLay::kScaleStride, c < nch);
+    if constexpr (kScaleDword) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q) r.s4[q] = ld_global<uint32_t>(ws4_src[q], (size_t)c * WLay::kScaleStride, c < nch);
+    }
   };
   // the E8M0 byte of tile t for this lane
   auto wscale = [&](const WeightRegs<WF, NT>& wr, int t) -> uint32_t {
     if constexpr (kScaleDword) {
-      const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * t + (lane >> 2)) << 2, (int)wr.s4);
+      const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (t % 4) + (lane >> 2)) << 2, (int)wr.s4[t / 4]);
       return (v >> (8 * (lane & 3))) & 0xFFu;
     } else {
       return wr.s[t];
@@ -383,13 +400,14 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   // buffers only (lds_barrier): a __syncthreads would also wait for every global load in
   // flight, i.e. drain the ring each chunk.
   // Ring depths measured on MI355X (prefill-sized batches): w4a16 0 (depth 1 is 40% slower,
-  // 2 within 1%), w4a4 2 (6% faster than 1), FP8 block 1 and FP8 channel 2 (one more
+  // 2 within 1%), w4a4 1 at six tiles per wave (2 spills there; at four tiles 2 was 6%
+  // faster than 1, and six tiles at depth 1 beat both), FP8 block 1 and FP8 channel 2 (one more
   // spills and runs ~3x slower).
 #ifndef MOE_PF_BF16
 #define MOE_PF_BF16 0
 #endif
 #ifndef MOE_PF_F4A4
-#define MOE_PF_F4A4 2
+#define MOE_PF_F4A4 1  // w4a4 at more than four tiles per wave (four tiles: 2)
 #endif
 #ifndef MOE_PF_F8B
 #define MOE_PF_F8B 1
@@ -398,7 +416,8 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
 #define MOE_PF_F8C 2
 #endif
   constexpr int kPF = (AF == kABf16) ? MOE_PF_BF16
-                                     : (AF == kAMxfp4 ? MOE_PF_F4A4 : (WF == kWFp8Channel ? MOE_PF_F8C : MOE_PF_F8B));
+                                     : (AF == kAMxfp4 ? (NT > 4 ? MOE_PF_F4A4 : 2)
+                                                      : (WF == kWFp8Channel ? MOE_PF_F8C : MOE_PF_F8B));
   auto chunk_barrier = [] { lds_barrier(); };
   // kDmaA: chunk c's A tile straight into LDS buffer buf (each wave's 64 pieces of a round
   // are 1 KB contiguous); rows past the batch and K past the end read the zero page
@@ -1609,7 +1628,8 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
     return hipErrorInvalidValue;  // bf16 weights: the persistent kernel or 64/128-row blocks only
   } else {
   // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
-  constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q) : (WF == kWBf16 ? 2 : 4);
+  constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q)
+                            : (WF == kWBf16 ? 2 : (AF == kAMxfp4 && BM == 64 ? MOE_NT_F4A4 : 4));
   if constexpr (kSplit) {
     // (one or two tokens leave CUs idle here, e.g. 128 workgroups for stage 2 of a 4096-wide
     // layer; strips of 2 or 1 tiles per wave that fill the chip measured 1-3% slower)

@@ -68,11 +68,12 @@ __device__ __forceinline__ float ld_uniform_f32(const float* ptr) {
   return *(const __attribute__((address_space(4))) float*)ptr;
 }
 
+constexpr int kScaleGroups = 2;  // scale dwords of WeightRegs: up to 8 tiles
 template <int WF, int NT>
 struct WeightRegs {
   i32x4 w[NT][WF == kWMxfp4 ? 1 : (WF == kWBf16 ? 4 : 2)];  // 16 B (MXFP4), 32 B (FP8), 64 B (bf16) per tile
   uint32_t s[NT];                      // MXFP4: E8M0 byte
-  uint32_t s4;                         // tiled MXFP4 (64/128-row kernel): 4 scale bytes, see kScaleDword
+  uint32_t s4[kScaleGroups];           // tiled MXFP4 (64/128-row kernel): 4 scale bytes per dword, see kScaleDword
   float sb[NT];                        // FP8 block: w_scale of this chunk
 };
 
