@@ -72,6 +72,11 @@ namespace moe {
 #ifndef MOE_NT_F4A4
 #define MOE_NT_F4A4 6
 #endif
+// ... and for stage 2 of w4a16 (each A fragment read from LDS feeds six tiles): prefill
+// (T = 8192) stage 2 596 against 617 us; stage 1 measured the same at four and six
+#ifndef MOE_NT_W4A16_S2
+#define MOE_NT_W4A16_S2 6
+#endif
 #ifndef MOE_KSPLIT_WGS_PER_CU
 #define MOE_KSPLIT_WGS_PER_CU 2
 #endif
@@ -1629,7 +1634,10 @@ static hipError_t launch_one_impl(const GemmParams& p_in, hipStream_t stream) {
   } else {
   // (bf16 weights: two tiles per wave, their 64 B per lane and chunk fill the registers)
   constexpr int NT = kSplit ? (AF == kABf16 ? MOE_KSPLIT_NT_BF16 : MOE_KSPLIT_NT_Q)
-                            : (WF == kWBf16 ? 2 : (AF == kAMxfp4 && BM == 64 ? MOE_NT_F4A4 : 4));
+                            : (WF == kWBf16 ? 2
+                                            : (BM != 64 ? 4
+                                                        : (AF == kAMxfp4 ? MOE_NT_F4A4
+                                                                         : (AF == kABf16 && STAGE == 2 ? MOE_NT_W4A16_S2 : 4))));
   if constexpr (kSplit) {
     // (one or two tokens leave CUs idle here, e.g. 128 workgroups for stage 2 of a 4096-wide
     // layer; strips of 2 or 1 tiles per wave that fill the chip measured 1-3% slower)
