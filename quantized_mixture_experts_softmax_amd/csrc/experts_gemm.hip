@@ -63,12 +63,11 @@ namespace moe {
 #ifndef MOE_LDS_GEMM  // 128-row blocks on tiled weights: the LDS-staged kernel of gemm_lds.hip
 #define MOE_LDS_GEMM 1
 #endif
-// Workgroups per CU the small-block launch is sized for (strips per workgroup grow
-// until the grid is about this many workgroups per CU).
-// Column tiles per wave of the 64-row kernel for w4a4 (4 for the other formats).  Six
-// tiles cut the activation bytes per flop through the vector-memory return path, which
-// bounds w4a4 here: prefill-w4a4 (T = 8192) 1.26 against 1.33 ms per step on MI355X
-// (stage 2 -13%, stage 1 -2.5%), at ring depth 1 (depth 2 spills at six tiles).
+// Column tiles per wave of the 64-row kernel for w4a4 (4 for the other formats, except
+// stage 2 of w4a16 below).  Six tiles cut the activation bytes per flop through the
+// vector-memory return path, which bounds w4a4 here: prefill-w4a4 (T = 8192) 1.26 against
+// 1.33 ms per step on MI355X (stage 2 -13%, stage 1 -2.5%), at ring depth 1 (depth 2
+// spills at six tiles).
 #ifndef MOE_NT_F4A4
 #define MOE_NT_F4A4 6
 #endif
@@ -77,6 +76,8 @@ namespace moe {
 #ifndef MOE_NT_W4A16_S2
 #define MOE_NT_W4A16_S2 6
 #endif
+// Workgroups per CU the small-block launch is sized for (strips per workgroup grow
+// until the grid is about this many workgroups per CU).
 #ifndef MOE_KSPLIT_WGS_PER_CU
 #define MOE_KSPLIT_WGS_PER_CU 2
 #endif
