@@ -329,6 +329,21 @@ moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream);
 moe_status moe_experts_forward_noalloc(const moe_forward_args* a, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * moe_set_checked_mode -- a debugging aid for callers that build the routing tables
+ * themselves.  With `on` nonzero (process-wide; off by default), moe_experts_forward and
+ * moe_experts_forward_noalloc first check, on the device, the tables the expert kernels
+ * index with: num_padded in [0, capacity] and a multiple of block_m; every sorted_slots
+ * entry below num_padded in [0, T*K] (T*K is the pad sentinel); every block_expert entry
+ * below num_padded / block_m in [-1, E_total).  The call then waits for the stream; tables
+ * that fail return MOE_EINVAL (moe_last_error() names the first entry found) with nothing
+ * further enqueued, so a corrupt table is reported instead of being read out of bounds.
+ * Each checked call costs one small kernel and a stream synchronisation, and is therefore
+ * not capturable in a HIP graph.  moe_layer_forward's fused small-batch path builds its
+ * tables inside the first GEMM kernel and is not checked.  Returns MOE_OK.
+ * ---------------------------------------------------------------------------------- */
+moe_status moe_set_checked_mode(int on);
+
+/* ------------------------------------------------------------------------------------
  * moe_layer_forward -- the whole layer from router logits: moe_route_align (E = E_total -
  * n_shared routed experts, topk = K - n_shared, the block_m of `a`) writing into the
  * routing buffers that `a` names, then moe_experts_forward(a).  The pages' layer takes

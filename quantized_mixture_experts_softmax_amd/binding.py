@@ -27,7 +27,7 @@ EXPORTED = [
     "moe_route_topk", "moe_route_grouped_topk", "moe_map_experts", "moe_sort_capacity", "moe_align_sort", "moe_route_align", "moe_quant_act",
     "moe_experts_workspace_bytes", "moe_workspace_layout", "moe_experts_forward", "moe_layer_forward",
     "moe_supports", "moe_pick_block_m", "moe_profile_events", "moe_last_error",
-    "moe_tiled_weight_bytes", "moe_tile_weights", "moe_experts_forward_noalloc",
+    "moe_tiled_weight_bytes", "moe_tile_weights", "moe_experts_forward_noalloc", "moe_set_checked_mode",
 ]
 # library-owned workspace of moe_experts_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.moe_pick_block_m.argtypes = [I, I, I, I, I]
         L.moe_profile_events.restype = S
         L.moe_profile_events.argtypes = [P, I]
+        L.moe_set_checked_mode.restype = S
+        L.moe_set_checked_mode.argtypes = [I]
         L.moe_tiled_weight_bytes.restype = ctypes.c_size_t
         L.moe_tiled_weight_bytes.argtypes = [I, I, I, I]
         L.moe_tile_weights.restype = S
@@ -146,6 +148,11 @@ def _dev(t: torch.Tensor) -> torch.device:
 
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
+
+
+def moe_set_checked_mode(on: bool) -> None:
+    """Forward calls verify caller-built routing tables on the device first (see moe.h)."""
+    _check(lib().moe_set_checked_mode(1 if on else 0))
 
 
 def moe_profile_events(events: list | None) -> None:

@@ -14,6 +14,8 @@
 // never names this array as an address: its device address comes from hipGetSymbolAddress
 // (scratch_ptr below).
 static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+// Checked mode: the verdict of the last table check on this device (code, entry index).
+static __device__ int32_t check_result[2];
 
 namespace {
 
@@ -345,6 +347,91 @@ size_t moe_experts_workspace_bytes(const moe_forward_args* a) {
 
 namespace {
 
+std::atomic<int> g_checked{0};  // moe_set_checked_mode
+
+// Checked mode: the routing tables a forward call reads, against the bounds its kernels
+// index with (the weights by block owner, the token rows and per-slot rows by slot).  One
+// workgroup; result[0] = 0 (valid) or the code of the first violation claimed (1: padded
+// total, 2: sorted slot, 3: block owner), result[1] = the offending value or entry.  Reads
+// only sorted[0, num_padded) and owner[0, num_padded / bm), after num_padded is checked
+// against the capacity the caller's buffers hold.
+__global__ __launch_bounds__(1024) void check_tables_kernel(const int32_t* __restrict__ sorted,
+                                                            const int32_t* __restrict__ owner,
+                                                            const int32_t* __restrict__ num_padded, int cap, int bm,
+                                                            int TK, int E, int32_t* __restrict__ result) {
+  __shared__ int code, where;
+  const int tid = (int)threadIdx.x;
+  const int np = num_padded[0];
+  if (tid == 0) {
+    const bool bad = np < 0 || np > cap || np % bm != 0;
+    code = bad ? 1 : 0;
+    where = np;
+  }
+  __syncthreads();
+  if (code == 0) {
+    for (int q = tid; q < np; q += (int)blockDim.x) {
+      const int s = sorted[q];
+      if ((s < 0 || s > TK) && atomicCAS(&code, 0, 2) == 0) where = q;
+    }
+    for (int b = tid; b < np / bm; b += (int)blockDim.x) {
+      const int e = owner[b];
+      if ((e < -1 || e >= E) && atomicCAS(&code, 0, 3) == 0) where = b;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    result[0] = code;
+    result[1] = where;
+  }
+}
+
+// Device address of check_result on the current device (looked up once per device).
+int32_t* check_result_ptr(hipError_t* err) {
+  static std::atomic<void*> ptrs[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_result));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  *err = hipSuccess;
+  return (int32_t*)p;
+}
+
+// Runs check_tables_kernel on the call's tables and waits for its verdict.
+moe_status check_tables(const moe_forward_args* a, size_t cap, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  int32_t* res = check_result_ptr(&e);
+  if (!res) return hip_status(e, "checked mode: result address");
+  check_tables_kernel<<<1, 1024, 0, stream>>>(a->sorted_slots, a->block_expert, a->num_padded, (int)cap, a->block_m,
+                                              a->T * a->K, a->E_total, res);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_status(e, "checked mode: table check launch");
+  int32_t host[2] = {0, 0};
+  if ((e = hipMemcpyAsync(host, res, sizeof host, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(stream)) != hipSuccess)
+    return hip_status(e, "checked mode: table check result");
+  switch (host[0]) {
+    case 0:
+      return ok();
+    case 1:
+      return fail(MOE_EINVAL, "checked mode: num_padded = %d, but it must be a multiple of block_m %d in [0, %zu]",
+                  host[1], a->block_m, cap);
+    case 2:
+      return fail(MOE_EINVAL, "checked mode: sorted_slots[%d] is outside [0, T*K = %d]", host[1], a->T * a->K);
+    default:
+      return fail(MOE_EINVAL, "checked mode: block_expert[%d] is outside [-1, E_total = %d)", host[1], a->E_total);
+  }
+}
+
 // Routing that stage 1 performs itself (moe_layer_forward on a small batch).
 struct FusedRoute {
   const float* logits;
@@ -379,6 +466,9 @@ moe_status experts_forward(const moe_forward_args* a, const FusedRoute* r, hipSt
 
   uint8_t* ws = (uint8_t*)a->workspace;
   const size_t cap = moe_sort_capacity(a->T, a->K, a->E_total, a->block_m);
+  // checked mode: caller-built tables are verified before anything reads them (the fused
+  // route builds its own in stage 1)
+  if (!r && g_checked.load(std::memory_order_relaxed) && (st = check_tables(a, cap, stream)) != MOE_OK) return st;
   const int afmt = (int)a->afmt;
   uint16_t* h = (uint16_t*)(ws + L.h_off);
   const void* a1 = a->hidden_states;
@@ -518,6 +608,11 @@ void* scratch_ptr(hipError_t* err) {
 }  // namespace
 
 extern "C" {
+
+moe_status moe_set_checked_mode(int on) {
+  g_checked.store(on ? 1 : 0, std::memory_order_relaxed);
+  return ok();
+}
 
 moe_status moe_experts_forward(const moe_forward_args* a, hipStream_t stream) {
   return experts_forward(a, nullptr, stream);

@@ -70,6 +70,8 @@ int main() {
   CHECK(moe_experts_forward(&z, nullptr) == MOE_EINVAL);
   CHECK(moe_profile_events(nullptr, 3) == MOE_EINVAL);
   CHECK(moe_profile_events(nullptr, 0) == MOE_OK);
+  CHECK(moe_set_checked_mode(1) == MOE_OK);  // host state only; the check itself runs on a forward call
+  CHECK(moe_set_checked_mode(0) == MOE_OK);
   CHECK(moe_last_error()[0] == '\0');
   printf("abi-sanitize ok\n");
   return 0;
