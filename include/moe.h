@@ -11,12 +11,13 @@
  *     row-major.  The library keeps no pointer after a call returns.
  *   - Calls only enqueue work on `stream` (NULL = the null stream).  They never
  *     allocate device memory, never synchronise the host and never read device
- *     data on the host, so a call may be captured into a HIP graph.
+ *     data on the host, so a call may be captured into a HIP graph.  (The one
+ *     exception is checked mode, off unless moe_set_checked_mode turns it on.)
  *   - Arguments are validated on the host before anything is enqueued.  On a
- *     non-MOE_OK status nothing was enqueued and moe_last_error() returns a
- *     message for the calling thread.  Invalid DEVICE data (an expert id out of
- *     range in topk_ids, NaN logits) is not an error: such slots are dropped as
- *     documented per call.
+ *     non-MOE_OK status nothing was enqueued (in checked mode: nothing after the
+ *     table check) and moe_last_error() returns a message for the calling thread.
+ *     Invalid DEVICE data (an expert id out of range in topk_ids, NaN logits) is not
+ *     an error: such slots are dropped as documented per call.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Results are deterministic: the same inputs give bit-identical outputs on
  *     every call (no floating-point atomics anywhere).
