@@ -19,7 +19,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off: the compiler may not form v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+    "-Wall",
 ]
 
 

@@ -164,7 +164,6 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void moe_gemm_kernel(const G
   }
 
   // ---- weight rows of this wave's tiles (lane li = column inside the tile) ----
-  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
   const int nbn = (p.Nw + 127) / 128, nbk = nch;
   const uint8_t* w_src[NT];
   const uint8_t* ws_src[NT];
@@ -664,7 +663,6 @@ __global__ __launch_bounds__(256) void moe_gemm_ksplit_kernel(const GemmParams p
   const int n_my = (nch + 3) / 4;  // chunk slots per wave and strip (the same for every wave)
   const int TK = p.T * p.slots_per_token;
   const size_t a_row_bytes = (AF == kABf16) ? (size_t)K * 2 : (AF == kAMxfp4 ? (size_t)K / 2 : (size_t)K);
-  const size_t w_row_bytes = (WF == kWMxfp4) ? (size_t)K / 2 : (size_t)K;
   const int nbn = (p.Nw + 127) / 128, nbk = nch;
 
   // Output column of this lane for tile t of strip s (stage 1 interleaved rows: the
